@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws inputs; it holds none of the attention arithmetic and
+is shared by the tests, the benchmark and the smoke check (the CPU oracle and
+the HIP library never import it).
+
+Recipe (the pages measure on synthetic kernel sweeps with unstated shapes, so
+no public dataset is involved):
+  * one CPU ``torch.Generator`` per workload, seeded by the workload's seed;
+  * draw order Q, K, V, then dO for the backward workload;
+  * each tensor is float32 N(0, 1) rounded to bf16 (round-to-nearest-even by
+    ``Tensor.to``), layout [B, H, S, d] contiguous;
+  * the rescale-stress workload adds, before rounding, a per-key bias along
+    the unit mean direction u of the (b, h) slice's queries:
+    k_j += (ramp * sqrt(d) * j / (Sk - 1)) * u, with ramp = 6 -- six standard
+    deviations of the raw score q.k (whose deviation is sqrt(d)) at the last
+    key, so row maxima keep rising and some rows cross tau = 8 (log2 units).
+"""
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    d: int
+    causal: bool
+    seed: int
+    kind: str = "fwd"               # "fwd" or "bwd" (bwd also runs fwd for O, LSE)
+    key_ramp: float = 0.0           # in standard deviations of q.k
+    emu_fracs: tuple = (0.0,)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, pass_="fwd"):
+        """Counted FLOPs: forward 4*B*H*Sq*Sk*d, backward 10*B*H*Sq*Sk*d;
+        causal counts half."""
+        per_pair = 4 if pass_ == "fwd" else 10
+        f = per_pair * self.B * self.H * self.Sq * self.Sk * self.d
+        return f / 2 if self.causal else f
+
+
+WORKLOADS = {
+    1: Workload("tiny-fwd-noncausal-B1H2S256d64", 1, 2, 256, 256, 64, False, seed=1),
+    2: Workload("fwd-noncausal-B2H16S2048d128", 2, 16, 2048, 2048, 128, False, seed=2),
+    3: Workload("fwd-causal-B1H16S8192d128", 1, 16, 8192, 8192, 128, True, seed=3),
+    4: Workload("fwd-causal-rescale-stress-B4H32S4096d64", 4, 32, 4096, 4096, 64, True, seed=4,
+                key_ramp=6.0, emu_fracs=(0.0, 0.10, 0.25)),
+    5: Workload("bwd-causal-B1H16S4096d128", 1, 16, 4096, 4096, 128, True, seed=5, kind="bwd"),
+}
+
+
+def make_inputs(B, H, Sq, Sk, d, seed, key_ramp=0.0, with_dout=False, heads=None):
+    """Draw bf16 Q, K, V (and dO) on the CPU.
+
+    ``heads``: optional (h0, h1) to return only that head range of the full
+    draw (the full tensors are drawn so a subset matches the full workload).
+    """
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, Sq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Sk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Sk, d), generator=g, dtype=torch.float32)
+    do = torch.randn((B, H, Sq, d), generator=g, dtype=torch.float32) if with_dout else None
+    if key_ramp:
+        u = q.mean(dim=2, keepdim=True)
+        u = u / u.norm(dim=-1, keepdim=True)
+        ramp = key_ramp * math.sqrt(d) * torch.arange(Sk, dtype=torch.float32) / max(1, Sk - 1)
+        k = k + ramp[None, None, :, None] * u
+    out = [q, k, v] + ([do] if with_dout else [])
+    if heads is not None:
+        out = [t[:, heads[0]:heads[1]] for t in out]
+    out = [t.to(torch.bfloat16).contiguous() for t in out]
+    return tuple(out)
+
+
+def workload_inputs(w, heads=None):
+    return make_inputs(w.B, w.H, w.Sq, w.Sk, w.d, w.seed, key_ramp=w.key_ramp,
+                       with_dout=(w.kind == "bwd"), heads=heads)
