@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = fa_fwd followed by fa_bwd (every step of the forward and the
+backward path) on the bwd workload: B=1, H=16, Sq=Sk=4096, d=128, causal,
+bf16 inputs drawn by workloads.py (seed 5), O and LSE taken from fa_fwd.
+Inputs and outputs are resident in device memory before timing starts.
+
+Printed: ONE JSON line with the throughput in TFLOP/s (counted FLOPs:
+forward 4*B*H*S^2*d, backward 10*B*H*S^2*d, causal counts half), its share
+of the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096
+FLOP/clk), a roofline entry for the dominant kernel, the CPU oracle timed on
+a bounded sample of the same workload, and per-kernel / per-workload
+details (including the long causal forward, B=1 H=16 S=8192 d=128).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=5, help="workload id in workloads.WORKLOADS")
+    p.add_argument("--tau", type=float, default=8.0)
+    p.add_argument("--emu", type=float, default=0.0)
+    p.add_argument("--deterministic", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the per-workload forward sweep")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
+    p.add_argument("--fwd-only", action="store_true")
+    p.add_argument("--reps", type=int, default=0, help="only run K steps (for profilers), print nothing else")
+    return p.parse_args()
+
+
+def time_calls(fn, n, warmup):
+    """Mean milliseconds of fn() over n calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle (fwd + bwd) on whole heads of the workload, until the
+    time budget is used; returns TFLOP/s of the same counted FLOPs."""
+    import numpy as np
+    from oracle import attention_backward, attention_forward
+    from workloads import workload_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    done, t_total = 0, 0.0
+    flops_per_head = (w.flops("fwd") + (w.flops("bwd") if w.kind == "bwd" else 0)) / (w.B * w.H)
+    for h in range(w.H):
+        ins = workload_inputs(w, heads=(h, h + 1))
+        t0 = time.perf_counter()
+        attention_forward(ins[0][:1], ins[1][:1], ins[2][:1], w.scale, w.causal)
+        if w.kind == "bwd":
+            attention_backward(ins[0][:1], ins[1][:1], ins[2][:1], ins[3][:1], w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(flops_per_head * done / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} (b,h) heads of {w.name}, float64 NumPy "
+                      f"{'fwd+bwd' if w.kind == 'bwd' else 'fwd'}, {t_total:.1f} s; "
+                      f"GEMMs on {threads} BLAS threads, exp/max single-threaded; "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
+              "single-GPU and the multi-GPU sharding is a design note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import exact_attention_50_amd as fa
+    from workloads import WORKLOADS, workload_inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    ins = [t.to(dev) for t in workload_inputs(w)]
+    q, k, v = ins[:3]
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    do = ins[3] if len(ins) > 3 else torch.randn_like(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, fa.fa_bwd_workspace_bytes(B, H, Sq, Sk, d, w.causal, args.deterministic)),
+                     dtype=torch.uint8, device=dev)
+    do_bwd = not args.fwd_only
+
+    def fwd():
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, tau=args.tau, emu_frac=args.emu)
+
+    def bwd():
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
+                  deterministic=bool(args.deterministic))
+
+    if args.reps:
+        for _ in range(args.reps):
+            fwd()
+            if do_bwd:
+                bwd()
+        torch.cuda.synchronize()
+        print(f"ran {args.reps} steps of {w.name}", flush=True)
+        return
+
+    # ---- warmup, then exactly K timed steps with per-kernel-call events
+    for _ in range(args.warmup):
+        fwd()
+        if do_bwd:
+            bwd()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        fwd()
+        e[1].record()
+        if do_bwd:
+            bwd()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if do_bwd else 0.0
+    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
+
+    f_fwd = w.flops("fwd")
+    f_bwd = w.flops("bwd") if do_bwd else 0.0
+    value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    kernels = {"fa_fwd": dict(ms=fwd_ms, flops=f_fwd)}
+    if do_bwd:
+        kernels["fa_bwd"] = dict(ms=bwd_ms, flops=f_bwd)
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    ach = kernels[dom]["flops"] / (kernels[dom]["ms"] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "flops_per_launch": kernels[dom]["flops"], "avg_launch_ms": round(kernels[dom]["ms"], 5)}
+
+    detail = {n: {"ms": round(x["ms"], 5), "tflops": round(x["flops"] / (x["ms"] * 1e-3) / 1e12, 2),
+                  "pct_peak": round(100 * x["flops"] / (x["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+              for n, x in kernels.items()}
+
+    extra = {}
+    if not args.no_extra:
+        for wid in (2, 3, 4):
+            ww = WORKLOADS[wid]
+            del_ins = [t.to(dev) for t in workload_inputs(ww)]
+            qq, kk, vv = del_ins[:3]
+            oo = torch.empty_like(qq)
+            ll = torch.empty(qq.shape[:3], dtype=torch.float32, device=dev)
+            for emu in ww.emu_fracs:
+                ms = time_calls(lambda: fa.fa_fwd(qq, kk, vv, oo, ll, causal=ww.causal, scale=ww.scale,
+                                                  tau=args.tau, emu_frac=emu), max(10, args.steps), 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}" + (f"-emu{emu:g}" if len(ww.emu_fracs) > 1 else "")] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                    "emu_realised": round(fa.fa_fwd_realised_emu_frac(ww.d, emu), 4)}
+            del del_ins, qq, kk, vv, oo, ll
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, workloads.py)",
+        "config": {"workload": w.name + ("" if do_bwd else " (forward only)"), "B": B, "H": H, "Sq": Sq,
+                   "Sk": Sk, "d": d, "causal": w.causal, "tau": args.tau, "emu_frac": args.emu,
+                   "deterministic_bwd": bool(args.deterministic),
+                   "step": "fa_fwd + fa_bwd" if do_bwd else "fa_fwd"},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "peak_tflops": PEAK_BF16_TFLOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": detail,
+        "workloads_fwd": extra,
+        "wall_s_timed": round(wall_s, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+"""Python binding of libfa, the gfx950 fused exact-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  PyTorch provides device
+memory and the current stream.  The functions named like the C entry points
+(``fa_fwd``, ``fa_bwd``, ...) take torch tensors and pass their device
+pointers through; ``forward`` / ``backward`` additionally allocate outputs.
+
+There is no fallback: if libfa.so is missing or a call fails, an exception is
+raised.
+"""
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError", "lib", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_exp2_probe",
+    "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "backward", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {fa_status_str(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "or python -m exact_attention_50_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, vp]
+    L.fa_fwd.restype = i
+    L.fa_fwd_realised_emu_frac.argtypes = [i, f]
+    L.fa_fwd_realised_emu_frac.restype = f
+    L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_bwd.restype = i
+    L.fa_exp2_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
+    L.fa_exp2_probe.restype = i
+    L.fa_status_str.argtypes = [i]
+    L.fa_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fa_status_str(status):
+    return lib().fa_status_str(int(status)).decode()
+
+
+def fa_fwd_realised_emu_frac(d, emu_frac):
+    return float(lib().fa_fwd_realised_emu_frac(int(d), float(emu_frac)))
+
+
+def fa_bwd_workspace_bytes(B, H, Sq, Sk, d, causal, deterministic):
+    return int(lib().fa_bwd_workspace_bytes(B, H, Sq, Sk, d, int(bool(causal)), int(bool(deterministic))))
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_bf16(name, t, shape):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous bf16 CUDA tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device} contiguous={t.is_contiguous()}")
+
+
+def _check_f32(name, t, shape):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous float32 CUDA tensor of shape {tuple(shape)}")
+
+
+# --------------------------------------------------------- C-named wrappers
+def fa_fwd(q, k, v, o, lse, causal=False, scale=None, tau=8.0, emu_frac=0.0):
+    """Enqueue the forward on the current stream; fills o and lse in place."""
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    _check_bf16("q", q, (B, H, Sq, d))
+    _check_bf16("k", k, (B, H, Sk, d))
+    _check_bf16("v", v, (B, H, Sk, d))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d, int(bool(causal)),
+                      float(scale), float(tau), float(emu_frac), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, deterministic=False):
+    """Enqueue the backward on the current stream; fills dq, dk, dv in place."""
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    for name, t, s in (("q", q, (B, H, Sq, d)), ("k", k, (B, H, Sk, d)), ("v", v, (B, H, Sk, d)),
+                       ("o", o, (B, H, Sq, d)), ("dout", dout, (B, H, Sq, d)), ("dq", dq, (B, H, Sq, d)),
+                       ("dk", dk, (B, H, Sk, d)), ("dv", dv, (B, H, Sk, d))):
+        _check_bf16(name, t, s)
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Sq, Sk, d, int(bool(causal)), float(scale), int(bool(deterministic)),
+                      _ptr(workspace), ws_bytes, _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+
+
+def fa_exp2_probe(x, y_hw, y_emu):
+    """Hardware and software 2^x of a float32 CUDA tensor, written in place."""
+    n = x.numel()
+    for name, t in (("x", x), ("y_hw", y_hw), ("y_emu", y_emu)):
+        _check_f32(name, t, (n,))
+    st = lib().fa_exp2_probe(_ptr(x), _ptr(y_hw), _ptr(y_emu), n, _stream(x))
+    if st != FA_OK:
+        raise FAError(st, "fa_exp2_probe")
+
+
+# ------------------------------------------------------ allocating helpers
+def forward(q, k, v, causal=False, scale=None, tau=8.0, emu_frac=0.0):
+    """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq])."""
+    import torch
+    B, H, Sq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, causal=causal, scale=scale, tau=tau, emu_frac=emu_frac)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=False, workspace=None):
+    """Returns (dQ, dK, dV) bf16."""
+    import torch
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if workspace is None:
+        nbytes = fa_bwd_workspace_bytes(B, H, Sq, Sk, d, causal, deterministic)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=causal, scale=scale,
+           deterministic=deterministic)
+    return dq, dk, dv

@@ -1,0 +1,105 @@
+// C ABI of the attention library: argument validation, then one launch
+// sequence on the caller's stream.  Declarations and contracts: include/fa.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool sizes_ok(int B, int H, int Sq, int Sk) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return false;
+  // index arithmetic uses size_t offsets per (b, h) slice and int row indices
+  const long long rows = (long long)B * H * (Sq > Sk ? Sq : Sk);
+  return rows < (1LL << 31);
+}
+
+bool d_supported(int d) { return d == FA_D_SMALL || d == FA_D_LARGE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+float fa_fwd_realised_emu_frac(int d, float emu_frac) {
+  if (!d_supported(d) || !(emu_frac >= 0.0f && emu_frac <= 1.0f)) return -1.0f;
+  return (float)fa::fwd_nearest_emu_count(d, emu_frac) / (float)fa::fwd_exps_per_lane_tile(d);
+}
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int Sq, int Sk,
+                 int d, int causal, float scale, float tau, float emu_frac, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 64.0f)) return FA_ERR_INVALID;
+  if (!(emu_frac >= 0.0f && emu_frac <= 1.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.tau = tau;
+  a.emu_count = fa::fwd_nearest_emu_count(d, emu_frac);
+  const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic) {
+  (void)causal;
+  if (!sizes_ok(B, H, Sq, Sk) || !d_supported(d)) return 0;
+  return fa::bwd_workspace_bytes(B, H, Sq, Sk, d, deterministic != 0);
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                 void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d, int causal, float scale,
+                 int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID;
+  const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (deterministic != 0 && deterministic != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, H, Sq, Sk, d, deterministic != 0)) return FA_ERR_INVALID;
+
+  fa::BwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE; a.dout = dO;
+  a.dq = dQ; a.dk = dK; a.dv = dV;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.deterministic = deterministic != 0;
+  a.workspace = workspace;
+  const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, void* stream) {
+  if (n < 0) return FA_ERR_INVALID;
+  if (n > 0 && (!x || !y_hw || !y_emu)) return FA_ERR_INVALID;
+  const hipError_t e = fa::launch_exp2_probe(x, y_hw, y_emu, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side building blocks shared by the forward and backward kernels
+// (gfx950 / CDNA4, wave64).
+//
+// MFMA lane layout used throughout (v_mfma_f32_32x32x16_bf16, checked on the
+// hardware): with lane l, g = l / 32 and r = l % 32,
+//   A (32 x 16, rows x k):  lane holds A[r][8g .. 8g+7]
+//   B (16 x 32, k x cols):  lane holds B[8g .. 8g+7][r]
+//   C (32 x 32):            lane holds C[8(i/4) + 4g + (i%4)][r], i = 0..15
+// so an accumulator column belongs to one lane pair (l, l^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "exp2_poly.h"
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Hardware 2^x (v_exp_f32).  -inf and inputs below the normal range give 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Software 2^x on the FMA pipes: Cody-Waite range reduction x = n + f with
+// n = floor(x), f in [0, 1); 2^f by a degree-3 minimax polynomial with
+// p(0) = 1 in Horner form (three FMAs); 2^n applied with ldexp.  Inputs below
+// -126 (and -inf) give exactly 0, as the hardware exponential does.
+// (FA4 paper §3.1.3, Table 2, as summarised on "FlashAttention-4: Algorithm
+// and Kernel Pipelining Co-Design for Asymmetric Hardware Scaling".)
+__device__ __forceinline__ float exp2_sw(float x) {
+  const float xc = __builtin_fmaxf(x, -127.0f);
+  const float f = __builtin_amdgcn_fractf(xc);
+  const int n = (int)__builtin_floorf(xc);
+  float p = __builtin_fmaf(FA_EXP2_D3_C3, f, FA_EXP2_D3_C2);
+  p = __builtin_fmaf(p, f, FA_EXP2_D3_C1);
+  p = __builtin_fmaf(p, f, 1.0f);
+  const float r = __builtin_amdgcn_ldexpf(p, n);
+  return x < -126.0f ? 0.0f : r;
+}
+
+// Exchange a value with the other half of the wave (lane l <-> l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// Round eight floats to bf16 (nearest-even) and pack them as an MFMA operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                              float a6, float a7) {
+  f32x8 v = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// Byte permutes that interleave the 16-bit halves of two words:
+// lo_pair(a, b) = {a.lo, b.lo}, hi_pair(a, b) = {a.hi, b.hi}.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+}  // namespace fa

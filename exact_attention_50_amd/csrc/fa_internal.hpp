@@ -1,0 +1,51 @@
+// Host-side interface between the C ABI (fa_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Sq, Sk, d;
+  bool causal;
+  float scale;
+  float tau;
+  int emu_count;  // exponentials per lane per tile computed in software
+};
+
+// Per-lane exponentials of one forward tile (BN keys x 32 queries / 64 lanes).
+int fwd_exps_per_lane_tile(int d);
+// Software-exponential counts the forward kernel is instantiated for.
+int fwd_nearest_emu_count(int d, float emu_frac);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Sq, Sk, d;
+  bool causal;
+  float scale;
+  bool deterministic;
+  void* workspace;
+};
+
+size_t bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, bool deterministic);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+hipError_t launch_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,114 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * What it computes.  Exact softmax attention, O = softmax(scale * Q K^T
+ * [+ causal mask]) V, and the per-row log-sum-exp, tile by tile with an
+ * online softmax so that neither the score matrix S nor the probabilities P
+ * ever reach device memory; and the gradients dQ, dK, dV of that function.
+ * The forward follows the FlashAttention-4 paper as summarised on the page
+ * "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for Asymmetric
+ * Hardware Scaling" (Key claims and Method): conditional rescaling of the
+ * running output with threshold tau (paper §3.1.4, Eq. 6) and a software
+ * 2^x (Cody-Waite range reduction + polynomial, paper §3.1.3, Table 2) for a
+ * share of the exponentials.  The backward recomputes P from the LSE and uses
+ * five matrix products per tile (paper §3.2.1, Eq. 7-8); its deterministic
+ * mode fixes the order of the dQ accumulation (paper §1).
+ *
+ * Conventions shared by every entry point.
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA
+ *     memory) on the current device.  bf16 tensors are passed as void* to
+ *     16-bit IEEE bfloat16 patterns.
+ *   - Layout: Q, O, dO, dQ are [B, H, Sq, d]; K, V, dK, dV are [B, H, Sk, d];
+ *     LSE is [B, H, Sq] float32 (natural log); all dense row-major
+ *     (contiguous, d fastest).  Pointers must be 16-byte aligned.
+ *   - Causal: key j is visible to query i iff j <= i (top-left aligned);
+ *     causal requires Sq == Sk.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no
+ *     state between calls and is thread-safe.  Work is enqueued on `stream`
+ *     (0 = the null stream) and calls return without synchronising;
+ *     asynchronous faults surface at the caller's next synchronisation.
+ *   - Errors: arguments are validated before any HIP call; on error nothing
+ *     is enqueued and no output is touched.  No C++ exception crosses the
+ *     ABI.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,      /* null pointer, bad size, bad scalar, misaligned pointer, small workspace */
+  FA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (d, causal Sq != Sk) */
+  FA_ERR_HIP = 3           /* the HIP runtime reported an error while launching */
+} fa_status;
+
+/* Head dimensions the kernels are built for. */
+#define FA_D_SMALL 64
+#define FA_D_LARGE 128
+
+/* Forward.  Q, K, V bf16 in; O bf16 out; LSE float32 out.
+ *   scale     > 0 and finite; multiplies Q K^T (usually 1/sqrt(d)).
+ *   tau       threshold of the conditional rescale in log2 units, 0 <= tau
+ *             <= 64 (8 = log2 256 is the paper's default, §3.1.4).  The
+ *             correction of the running output is skipped while a row's max
+ *             (in log2 units) rises by at most tau over the max currently
+ *             applied; tau = 0 is the eager online softmax.  Exact after the
+ *             final normalisation for every tau.
+ *   emu_frac  share of the exponentials computed by the software 2^x
+ *             instead of the hardware one, 0 <= emu_frac <= 1 (the paper's
+ *             10-25 %, §3.1.3).  Realised as a fixed count of each lane's
+ *             per-tile exponentials, the supported count nearest emu_frac;
+ *             fa_fwd_realised_emu_frac() reports the share actually used.
+ *   B, H, Sq, Sk >= 1; d in {64, 128}.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H, int Sq, int Sk, int d, int causal, float scale,
+                 float tau, float emu_frac, void* stream);
+
+/* The share of exponentials fa_fwd computes in software for a requested
+ * emu_frac (a pure function of its arguments; no HIP call). Negative when
+ * the arguments are invalid. */
+float fa_fwd_realised_emu_frac(int d, float emu_frac);
+
+/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
+ * [B,H,Sq,d], the row terms D_i = sum_c dO_ic O_ic [B,H,Sq] float32, and the
+ * per-block turn counters of the deterministic mode.  0 on invalid sizes. */
+size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic);
+
+/* Backward.  Q, K, V, O, dO bf16 and LSE float32 in (O and LSE as written
+ * by fa_fwd on the same inputs); dQ, dK, dV bf16 out.  P is recomputed from
+ * LSE as exp(scale q.k - LSE); fp32 accumulation; outputs rounded to bf16
+ * (nearest-even) once.
+ *   deterministic  0: dQ contributions of different key blocks are added
+ *                  with float atomics (order varies run to run).
+ *                  1: they are added in ascending key-block order (a
+ *                  per-query-block turn counter gates each addition), so
+ *                  results are bit-identical run to run.
+ *   workspace      device memory of at least fa_bwd_workspace_bytes(...);
+ *                  its contents on entry do not matter (it is cleared on
+ *                  `stream`); it must not be used concurrently by another
+ *                  call.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 const void* dO, void* dQ, void* dK, void* dV,
+                 int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Element-wise probe of the two exponentials the forward uses, so their
+ * agreement can be measured (paper §3.1.3, Table 2): y_hw[i] = hardware
+ * 2^x[i] (v_exp_f32), y_emu[i] = the software 2^x[i] of the forward kernel.
+ * x, y_hw, y_emu are device float32 arrays of n >= 0 elements. */
+fa_status fa_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* fa_status_str(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H_ */

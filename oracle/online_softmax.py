@@ -20,9 +20,13 @@ Readings (listed in DESIGN.md):
   * "m_{j-1}" is the reference max currently applied (not the previous
     block's running max), strict test m_new - m_ref > tau, and the first
     block always sets m_ref;
-  * gating: rows are taken in consecutive groups of ``group_rows`` (one warp /
-    wavefront); if any row of a group needs the correction the whole group
-    moves each row to its own current maximum (factor 1 where unchanged);
+  * gating "at warp granularity": rows are taken in consecutive groups of
+    ``group_rows`` (one warp / wavefront); the correction step runs for a
+    group when any of its rows needs it, and inside it only the rows whose
+    max rose by more than tau move their reference (the others are multiplied
+    by exactly 1).  The arithmetic of each row therefore depends on that row
+    alone; the group size only changes how often the step runs
+    (``group_events``);
   * LSE = (m_ref + log2 l) * ln 2.
 """
 import numpy as np
@@ -38,8 +42,8 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
     """Tile-by-tile forward with conditional rescaling.
 
     Returns (O, LSE, stats).  stats holds, over all (b, h):
-      row_rescales   int array [B,H,Sq]: corrections applied to a row whose own
-                     max rose, after its first block
+      row_rescales   int array [B,H,Sq]: corrections applied to a row (its max
+                     rose by more than tau), after its first block
       group_events   number of (group, block) corrections after the first block
       rising_steps   number of (row, block) steps where the row max rose,
                      after the first block
@@ -78,16 +82,17 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
                     g = slice(g0, min(g0 + group_rows, Sq))
                     if not need[g].any():
                         continue
+                    ng = need[g]
                     if blk > 0:
                         group_events += 1
-                        row_rescales[b, h, g] += (m_new[g] > m_ref[g])
+                        row_rescales[b, h, g] += ng
                     with np.errstate(invalid="ignore"):
                         alpha = np.where(np.isfinite(m_ref[g]),
                                          np.exp2(m_ref[g] - m_new[g]), 0.0)
-                    alpha = np.where(np.isneginf(m_new[g]), 1.0, alpha)
+                    alpha = np.where(ng, alpha, 1.0)
                     acc[g] *= alpha[:, None]
                     l[g] *= alpha
-                    m_ref[g] = m_new[g]
+                    m_ref[g] = np.where(ng, m_new[g], m_ref[g])
                 with np.errstate(invalid="ignore"):
                     p = np.exp2(s - m_ref[:, None])
                 p[np.isnan(p)] = 0.0                    # -inf - -inf: no key yet

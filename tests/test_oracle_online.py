@@ -81,3 +81,15 @@ def test_stale_reference_gives_wrong_unnormalised_sum_without_final_division():
     q, k, v = _inputs(5, ramp=6.0)
     _, _, st8 = conditional_rescale_forward(q, k, v, 0.25, tau=8.0, block_n=16)
     assert st8["max_p"] > 1.0     # some probability was taken against a stale max
+
+
+def test_group_size_changes_event_count_only():
+    """Wave-gated correction with per-row selection: the same rows are
+    corrected whatever the group size; larger groups run the step in fewer
+    (group, block) events than there are row corrections."""
+    q, k, v = _inputs(6, S=256, ramp=6.0)
+    O1, L1, s1 = conditional_rescale_forward(q, k, v, 0.25, causal=True, tau=4.0, block_n=32, group_rows=1)
+    O32, L32, s32 = conditional_rescale_forward(q, k, v, 0.25, causal=True, tau=4.0, block_n=32, group_rows=32)
+    assert np.array_equal(s1["row_rescales"], s32["row_rescales"])
+    assert np.array_equal(O1, O32) and np.array_equal(L1, L32)
+    assert s32["group_events"] <= s1["group_events"] == s1["row_rescales"].sum()
