@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
     p.add_argument("--fwd-only", action="store_true")
     p.add_argument("--reps", type=int, default=0, help="only run K steps (for profilers), print nothing else")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="only run --reps plain device copies of this many MiB (scales HBM counters)")
     return p.parse_args()
 
 
@@ -126,6 +128,14 @@ def main():
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
                   deterministic=bool(args.deterministic))
 
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.reps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_mib} MiB x {max(1, args.reps)}", flush=True)
+        return
     if args.reps:
         for _ in range(args.reps):
             fwd()

@@ -72,4 +72,13 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// MFMA k-slot order.  In the C layout a lane holds, for i = 8h + j, the row
+// 16h + 8(j/4) + 4g + (j%4); used as a B operand (k-slot 8g + j) the rows of
+// each 16-row group therefore arrive with bits 2 and 3 of the offset
+// swapped.  Tensors staged in LDS as the matching A operand store each
+// group's 4-row quads at this position.
+__device__ __forceinline__ int quad_slot(int quad_in_group) {
+  return ((quad_in_group & 1) << 1) | ((quad_in_group >> 1) & 1);
+}
+
 }  // namespace fa

@@ -68,12 +68,6 @@ struct FwdLayout {
   static_assert(kKChunks % kThreads == 0, "K tile must split evenly");
 };
 
-// Position of key offset o (0..15) inside its 16-key group of the V^T rows:
-// bits 2 and 3 swapped, matching the key order of the S^T accumulator.
-__device__ __forceinline__ int vt_chunk_pos(int quad_in_group) {
-  return ((quad_in_group & 1) << 1) | ((quad_in_group >> 1) & 1);
-}
-
 template <int D>
 struct TileRegs {
   u32x4 k[FwdLayout<D>::kKPerThread];
@@ -122,7 +116,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16*
     if (u < L::kVUnits) {
       const int kq = u % (kBN / 4);
       const int dq = u / (kBN / 4);
-      const int col = 16 * (kq / 4) + 4 * vt_chunk_pos(kq % 4);
+      const int col = 16 * (kq / 4) + 4 * quad_slot(kq % 4);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // word w of each key row holds dims 8dq+2w (low half) and 8dq+2w+1 (high half)
