@@ -56,6 +56,41 @@ __device__ __forceinline__ float exp2_sw(float x) {
 // Exchange a value with the other half of the wave (lane l <-> l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of a value over the lane pair (l, l ^ 32), without LDS: after
+// v_permlane32_swap the two results hold x[l % 32] and x[l % 32 + 32].
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base`: raw buffer loads beyond it
+// return zeros, which replaces per-lane bounds branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane s supplies
+// the address of 4 consecutive 16-bit values of row s/4, columns 4(s%4)..+3
+// of a 4 x 16 block; lane i receives column i of the block, rows 0..3.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4_t*)(lds_addr));
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only (global
+// prefetches stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Round eight floats to bf16 (nearest-even) and pack them as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
                                               float a6, float a7) {

@@ -11,23 +11,27 @@
 // the result exact.
 //
 // CDNA4 mapping (ours, not the pages'):
-//   * workgroup = 4 wavefronts x 32 query rows = 128 rows; grid over
-//     (query block, head, batch), heaviest causal blocks first;
+//   * workgroup = 8 wavefronts x 32 query rows = 256 rows, one per CU; grid
+//     over (query block, head, batch), heaviest causal blocks first;
+//   * ping-pong: waves 0-3 and 4-7 form two groups with one wave of each on
+//     every SIMD; the groups alternate between a matrix phase (O += V P of
+//     the previous tile, then S of the next tile) and a vector phase (the
+//     softmax of that tile), one workgroup barrier per phase, so one SIMD's
+//     matrix core works for one wave while the other wave runs its softmax
+//     (the role split that the pages give to separate warpgroups);
 //   * S is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     Q^T is the B operand held in registers for the whole loop, K comes from
-//     LDS as the A operand; each lane then owns 16 scores of ONE query per
-//     32-key block, so the row max / sum need one exchange between the two
-//     halves of the wave only (the analogue of the pages' one-thread-one-row
-//     softmax);
+//     Q^T is the B operand kept in registers, K the A operand from LDS; each
+//     lane owns 16 scores of ONE query per 32-key block, so the row max / sum
+//     need one v_permlane32_swap between the wave halves;
 //   * O^T = V^T P^T: the S^T accumulator, rounded to bf16, is already the B
-//     operand (with the keys of each 16-key group in a fixed permuted order);
-//     V is transposed into LDS on the way in, in the same permuted order, so
-//     the A operand is one 16-byte LDS read per lane;
-//   * K and V tiles are double-buffered in LDS; the next tile's global loads
-//     are issued before the current tile's math and written to the other
-//     buffer after it, one barrier per tile;
-//   * LDS rows are padded by 16 bytes so the 16-byte MFMA operand reads of
-//     32 consecutive rows hit distinct banks.
+//     operand (keys of each 16-key group in a fixed permuted order); the V^T
+//     A operand is read from row-major V in LDS with ds_read_b64_tr_b16;
+//   * K / V tiles: 4-stage LDS ring, XOR-swizzled at 16-byte granularity so
+//     the MFMA operand reads are bank-conflict free; each tile is fetched to
+//     registers one matrix phase ahead and written to LDS one phase later;
+//     buffer descriptors bound every head, so rows past the end read zeros.
+
+#include <type_traits>
 
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
@@ -35,11 +39,12 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;               // query rows per wavefront
 constexpr int kBM = kWaves * kQW;     // query rows per workgroup
 constexpr int kBN = 64;               // keys per tile
+constexpr int kStages = 4;
 
 struct FwdParams {
   const bf16* q;
@@ -56,219 +61,363 @@ struct FwdParams {
 
 template <int D>
 struct FwdLayout {
-  static constexpr int kKStride = D + 8;        // bf16 per K row in LDS
-  static constexpr int kVStride = kBN + 8;      // bf16 per V^T row in LDS
-  static constexpr int kKElems = kBN * kKStride;
-  static constexpr int kVElems = D * kVStride;
-  static constexpr int kStageElems = kKElems + kVElems;
-  static constexpr int kKChunks = kBN * D / 8;  // 16-byte chunks of a K tile
-  static constexpr int kKPerThread = kKChunks / kThreads;
-  static constexpr int kVUnits = (kBN / 4) * (D / 8);   // 4 keys x 8 dims each
-  static constexpr int kVPerThread = (kVUnits + kThreads - 1) / kThreads;
-  static_assert(kKChunks % kThreads == 0, "K tile must split evenly");
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kRowsPerLoad = 64 / kChunks;        // rows of one wave-wide 16-byte load
+  static constexpr int kLoadsPerWave = kBN / kRowsPerLoad / kWaves;
+  static_assert(kLoadsPerWave >= 1, "tile too small for the workgroup");
 };
+
+// 16-byte chunk position of chunk c of row r (bank-conflict-free reads: K by
+// 32 rows at one chunk, V by ds_read_b64_tr_b16 over 4 rows x 4 chunks).
+template <int D>
+__device__ __forceinline__ int k_pos(int r, int c) {
+  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int v_pos(int r, int c) {
+  return D == 128 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
+}
 
 template <int D>
 struct TileRegs {
-  u32x4 k[FwdLayout<D>::kKPerThread];
-  u32x4 v[FwdLayout<D>::kVPerThread][4];
+  u32x4 k[FwdLayout<D>::kLoadsPerWave];
+  u32x4 v[FwdLayout<D>::kLoadsPerWave];
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const bf16* kh, const bf16* vh, int k0, int Sk,
-                                          int tid) {
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int k0, int wave, int lane) {
   using L = FwdLayout<D>;
 #pragma unroll
-  for (int i = 0; i < L::kKPerThread; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / (D / 8);
-    const int col = (c % (D / 8)) * 8;
-    const int key = k0 + row;
-    r.k[i] = key < Sk ? *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + col) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int i = 0; i < L::kVPerThread; ++i) {
-    const int u = tid + i * kThreads;
-    const int kq = u % (kBN / 4);
-    const int dq = u / (kBN / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * kq + j;
-      const bool ok = (u < L::kVUnits) && key < Sk;
-      r.v[i][j] = ok ? *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + 8 * dq) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < L::kLoadsPerWave; ++i) {
+    const int row = (i * kWaves + wave) * L::kRowsPerLoad + lane / L::kChunks;
+    const unsigned off = (unsigned)(k0 + row) * L::kRowBytes + (lane % L::kChunks) * 16;
+    r.k[i] = load16(rk, off);
+    r.v[i] = load16(rv, off);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16* vt, int tid) {
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* stage, int wave, int lane) {
   using L = FwdLayout<D>;
 #pragma unroll
-  for (int i = 0; i < L::kKPerThread; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / (D / 8);
-    const int col = (c % (D / 8)) * 8;
-    *reinterpret_cast<u32x4*>(ks + row * L::kKStride + col) = r.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < L::kVPerThread; ++i) {
-    const int u = tid + i * kThreads;
-    if (u < L::kVUnits) {
-      const int kq = u % (kBN / 4);
-      const int dq = u / (kBN / 4);
-      const int col = 16 * (kq / 4) + 4 * quad_slot(kq % 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // word w of each key row holds dims 8dq+2w (low half) and 8dq+2w+1 (high half)
-        const uint32_t a = r.v[i][0][w], b = r.v[i][1][w], c2 = r.v[i][2][w], d2 = r.v[i][3][w];
-        u32x2 even = {lo_pair(a, b), lo_pair(c2, d2)};
-        u32x2 odd = {hi_pair(a, b), hi_pair(c2, d2)};
-        *reinterpret_cast<u32x2*>(vt + (8 * dq + 2 * w) * L::kVStride + col) = even;
-        *reinterpret_cast<u32x2*>(vt + (8 * dq + 2 * w + 1) * L::kVStride + col) = odd;
-      }
-    }
+  for (int i = 0; i < L::kLoadsPerWave; ++i) {
+    const int row = (i * kWaves + wave) * L::kRowsPerLoad + lane / L::kChunks;
+    const int c = lane % L::kChunks;
+    *reinterpret_cast<u32x4*>(stage + row * L::kRowBytes + k_pos<D>(row, c) * 16) = r.k[i];
+    *reinterpret_cast<u32x4*>(stage + L::kTileBytes + row * L::kRowBytes + v_pos<D>(row, c) * 16) = r.v[i];
   }
 }
 
+constexpr int kAhead = 6;   // MFMA operands in flight per wave
+
+// LDS operand addressing.  With the XOR swizzles above, the byte offset of
+// every MFMA operand read factors into a per-lane base XOR a small constant
+// plus a constant, so each read needs one base register and an immediate:
+//
+//  K (A operand of S^T = K Q^T; rows 32 kb + r, dims 16 kc + 8 g .. +8):
+//    off = (k_lane ^ 32 kc) + 32 kb * RowBytes
+//    with k_lane = r RowBytes + 32 (x >> 1) + 16 (g ^ (x & 1)), x the row's
+//    swizzle key (r & 15 for d = 128, (r >> 1) & 7 for d = 64);
+//  V^T (A operand of O^T = V^T P^T; dims 32 db .. +32, keys of step ks, read
+//  as two ds_read_b64_tr_b16 of 4 keys x 16 dims, half jh):
+//    off = (v_lane ^ 64 db) + (16 ks + 8 jh) RowBytes
+//    with s = lane % 16, w the swizzle bit(s) of the lane's key
+//    ((s >> 2) & 3 for d = 128, (s >> 3) & 1 for d = 64),
+//    v_lane = (4 g + (s >> 2)) RowBytes + 64 w + 16 (2 ((lane >> 4) & 1)
+//             + ((s & 3) >> 1)) + 8 (s & 1).
+// The 16 keys of step ks arrive in the accumulator's order: slot 8 g + j
+// holds key 8 (j / 4) + 4 g + j % 4.
+template <int D>
+__device__ __forceinline__ int k_lane_offset(int lane) {
+  using L = FwdLayout<D>;
+  const int r = lane & 31, g = lane >> 5;
+  const int x = D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return r * L::kRowBytes + 32 * (x >> 1) + 16 * (g ^ (x & 1));
+}
+template <int D>
+__device__ __forceinline__ int v_lane_offset(int lane) {
+  using L = FwdLayout<D>;
+  const int s16 = lane & 15, g = lane >> 5;
+  const int w = D == 128 ? ((s16 >> 2) & 3) : ((s16 >> 3) & 1);
+  return (4 * g + (s16 >> 2)) * L::kRowBytes + 64 * w + 16 * (2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1)) +
+         8 * (s16 & 1);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 read_k(const char* kst, int k_lane, int kb, int kc) {
+  using L = FwdLayout<D>;
+  return *reinterpret_cast<const bf16x8*>(kst + (k_lane ^ (32 * kc)) + 32 * kb * L::kRowBytes);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 read_vt(const char* vst, int v_lane, int ks, int db) {
+  using L = FwdLayout<D>;
+  const char* base = vst + (v_lane ^ (64 * db)) + 16 * ks * L::kRowBytes;
+  const bf16x4_t lo = lds_read_tr16(base);
+  const bf16x4_t hi = lds_read_tr16(base + 8 * L::kRowBytes);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 template <int D, bool CAUSAL, int EMU>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   using L = FwdLayout<D>;
   constexpr int kKB = kBN / 32;   // 32-key blocks per tile
+  constexpr int kKS = kBN / 16;   // 16-key steps of P V
   constexpr int kDB = D / 32;     // 32-dim blocks of the output
   constexpr int kKC = D / 16;     // 16-dim steps of Q K^T
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * L::kStageElems];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  // heaviest causal query blocks are launched first; heads interleave so the
-  // blocks of one head share an XCD's L2 (workgroups go round-robin to XCDs)
+  // heaviest causal query blocks first; consecutive workgroups take different
+  // heads of the same block rank
   const int rank = blockIdx.x / p.BH;
   const int bh = blockIdx.x % p.BH;
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
 
-  const bf16* qh = p.q + (size_t)bh * p.Sq * D;
-  const bf16* kh = p.k + (size_t)bh * p.Sk * D;
-  const bf16* vh = p.v + (size_t)bh * p.Sk * D;
+  const unsigned head_q = (unsigned)p.Sq * L::kRowBytes;
+  const unsigned head_k = (unsigned)p.Sk * L::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * D, head_q);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
 
   const int q_wave_lo = qb * kBM + wave * kQW;
   const int q_lane = q_wave_lo + r32;
+  const int k_lane = k_lane_offset<D>(lane);
+  const int v_lane = v_lane_offset<D>(lane);
 
-  // Q^T operand: lane holds Q[q_lane][16 kc + 8 g .. +8]
+  // Q^T operand: lane holds Q[q_lane][16 kc + 8 g .. +8] (zeros past the end)
   bf16x8 qf[kKC];
 #pragma unroll
-  for (int kc = 0; kc < kKC; ++kc) {
-    if (q_lane < p.Sq) {
-      qf[kc] = *reinterpret_cast<const bf16x8*>(qh + (size_t)q_lane * D + kc * 16 + 8 * g);
-    } else {
-      qf[kc] = bf16x8{};
-    }
-  }
+  for (int kc = 0; kc < kKC; ++kc)
+    qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, (unsigned)q_lane * L::kRowBytes + (kc * 16 + 8 * g) * 2));
 
   const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM) : p.Sk;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int n = (kv_end + kBN - 1) / kBN;
+  // tiles this wave needs: causal stops at the wave's last row
+  const int n_wave = CAUSAL ? min(n, (q_wave_lo + kQW - 1) / kBN + 1) : n;
 
   f32x16 o[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
+  f32x16 s[kKB];
+  bf16x8 pk[kKS];
   float m_ref = kNegInf;
-  float l_part = 0.0f;
+  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // 4 partial row sums
 
-  TileRegs<D> regs;
-  load_tile<D>(regs, kh, vh, 0, p.Sk, tid);
-  store_tile<D>(regs, smem, smem + L::kKElems, tid);
-  __syncthreads();
+  // ---- matrix phase: O += V_{t-1} P_{t-1}, then S_t = K_t Q^T, as one stream
+  // of MFMAs whose LDS operands are read kAhead MFMAs ahead through a small
+  // register ring; scheduling fences keep the compiler from hoisting all of
+  // them (which would not fit the register budget of two waves per SIMD).
+  constexpr int kNV = kKS * kDB;    // P V products
+  constexpr int kNK = kKB * kKC;    // K Q^T products
+  auto matrix_stream = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value;
+    constexpr bool SK = decltype(with_s)::value;
+    constexpr int j0 = PV ? 0 : kNV;
+    constexpr int j1 = SK ? kNV + kNK : kNV;
+    const char* vst = smem + ((t + kStages - 1) % kStages) * L::kStageBytes + L::kTileBytes;
+    const char* kst = smem + (t % kStages) * L::kStageBytes;
+    // j < kNV: (ks, db) = (j / kDB, j % kDB); j >= kNV: (kc, kb) = (i / kKB, i % kKB), i = j - kNV
+    auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      if (j < kNV) return read_vt<D>(vst, v_lane, j / kDB, j % kDB);
+      const int i = j - kNV;
+      return read_k<D>(kst, k_lane, i % kKB, i / kKB);
+    };
+    if (SK) {
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) s[kb] = f32x16{};
+    }
+    bf16x8 ring[kAhead];
+#pragma unroll
+    for (int j = j0; j < j0 + kAhead && j < j1; ++j) ring[(j - j0) % kAhead] = operand(j);
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const bf16x8 a = ring[(j - j0) % kAhead];
+      if (j + kAhead < j1) ring[(j - j0) % kAhead] = operand(j + kAhead);
+      if (j < kNV) {
+        o[j % kDB] = mfma32x32x16(a, pk[j / kDB], o[j % kDB]);
+      } else {
+        const int i = j - kNV;
+        s[i % kKB] = mfma32x32x16(a, qf[i / kKB], s[i % kKB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto matrix_s = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(t, std::false_type{}, std::true_type{});
+  };
+  auto matrix_full = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(t, std::true_type{}, std::true_type{});
+  };
+  auto matrix_pv = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(t, std::true_type{}, std::false_type{});
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    bf16* ks = smem + (t & 1) * L::kStageElems;
-    bf16* vt = ks + L::kKElems;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile<D>(regs, kh, vh, (t + 1) * kBN, p.Sk, tid);
-
+  // ---- vector phase: softmax of tile t
+  auto vector = [&](int t) __attribute__((always_inline)) {
+    if (t >= n_wave) return;
     const int k0 = t * kBN;
-    const bool active = !CAUSAL || k0 <= q_wave_lo + kQW - 1;
-    if (active) {
-      // ---- S^T = K Q^T for this tile: lane holds 16 keys per 32-key block
-      f32x16 s[kKB];
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        s[kb] = f32x16{};
-        const bf16* krow = ks + (kb * 32 + r32) * L::kKStride + 8 * g;
-#pragma unroll
-        for (int kc = 0; kc < kKC; ++kc) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kc * 16);
-          s[kb] = mfma32x32x16(a, qf[kc], s[kb]);
-        }
-      }
-      // ---- mask keys past the end and (causal) keys after the query
-      const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= p.Sk || (CAUSAL && key > q_lane)) s[kb][i] = kNegInf;
-          }
-      }
-      // ---- row max: within the lane, then across the two wave halves
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
-      mx = __builtin_fmaxf(mx, swap_halves(mx));
-      const float m_tile = mx * p.scale_log2;
-      const float m_new = __builtin_fmaxf(m_ref, m_tile);
-      // ---- conditional rescale: the branch is taken per wavefront (no
-      // divergence); inside it only the rows whose max rose by more than tau
-      // move their reference, the others multiply by exactly 1
-      const bool need = (m_new - m_ref) > p.tau;   // first tile: +inf > tau
-      if (__any(need)) {
-        const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;   // exp2(-inf) = 0
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) o[db] *= alpha;
-        m_ref = need ? m_new : m_ref;
-      }
-      // ---- P = 2^(s * scale_log2 - m_ref); a fixed share in software
-      const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
+    const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float x = __builtin_fmaf(s[kb][i], p.scale_log2, neg_m);
-          const float e = (kb * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
-          s[kb][i] = e;
-          l_part += e;
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= p.Sk || (CAUSAL && key > q_lane)) s[kb][i] = kNegInf;
         }
-      // ---- O^T += V^T P^T
+    }
+    // row max: 8 independent chains, then a short tree
+    float m8[8];
 #pragma unroll
-      for (int ks16 = 0; ks16 < kBN / 16; ++ks16) {
-        const int kb = ks16 >> 1, h = (ks16 & 1) * 8;
-        const bf16x8 b = pack_bf16x8(s[kb][h + 0], s[kb][h + 1], s[kb][h + 2], s[kb][h + 3], s[kb][h + 4],
-                                     s[kb][h + 5], s[kb][h + 6], s[kb][h + 7]);
-        const bf16* vrow = vt + r32 * L::kVStride + ks16 * 16 + 8 * g;
+    for (int c = 0; c < 8; ++c) m8[c] = s[0][c];
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + db * 32 * L::kVStride);
-          o[db] = mfma32x32x16(a, b, o[db]);
-        }
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int i = (kb == 0 ? 8 : 0); i < 16; ++i) m8[i & 7] = __builtin_fmaxf(m8[i & 7], s[kb][i]);
+    float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
+                               __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
+    mx = pair_max(mx);
+    const float m_new = __builtin_fmaxf(m_ref, mx * p.scale_log2);
+    // conditional rescale: wave-uniform branch; only rows whose max rose by
+    // more than tau move their reference, the others multiply by exactly 1
+    const bool need = (m_new - m_ref) > p.tau;   // first tile: +inf > tau
+    if (__any(need)) {
+      const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;   // exp2(-inf) = 0
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+      m_ref = need ? m_new : m_ref;
+    }
+    const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = __builtin_fmaf(s[kb][i], p.scale_log2, neg_m);
+        const float e = (kb * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
+        s[kb][i] = e;
+        l_part[i & 3] += e;
       }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const int kb = ks >> 1, h = (ks & 1) * 8;
+      pk[ks] = pack_bf16x8(s[kb][h + 0], s[kb][h + 1], s[kb][h + 2], s[kb][h + 3], s[kb][h + 4], s[kb][h + 5],
+                           s[kb][h + 6], s[kb][h + 7]);
     }
+  };
 
-    if (has_next) {
-      bf16* ks_n = smem + ((t + 1) & 1) * L::kStageElems;
-      store_tile<D>(regs, ks_n, ks_n + L::kKElems, tid);
+  TileRegs<D> regs;
+  auto fetch = [&](int u) __attribute__((always_inline)) {
+    if (u < n) load_tile<D>(regs, rk, rv, u * kBN, wave, lane);
+  };
+  auto commit = [&](int u) __attribute__((always_inline)) {
+    if (u < n) store_tile<D>(regs, smem + (u % kStages) * L::kStageBytes, wave, lane);
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  fetch(0);
+  commit(0);
+  fetch(1);
+  commit(1);
+  barrier();
+
+  // Phase schedule (interval k = 1 .. 2n+2, one workgroup barrier after each):
+  //   group 0: interval 2t+1 matrix(t), 2t+2 vector(t); 2n+1 matrix(n); 2n+2 idle
+  //   group 1: interval 1 idle; 2t+2 matrix(t), 2t+3 vector(t); 2n+2 matrix(n)
+  // matrix(t) = O += V_{t-1} P_{t-1} (t > 0) and S_t = K_t Q^T (t < n_wave);
+  // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
+  // n_wave - 1 but keeps taking part in the barriers.  Every wave fetches
+  // tile u into registers in interval 2u-3 and writes it to stage u % 4 at the
+  // end of interval 2u-2; tile u is read in intervals 2u+1 .. 2u+4.  Each
+  // variant of the matrix phase appears in a straight-line position of its
+  // own so the accumulators are never merged across branches.
+  if (group == 0) {
+    fetch(2);
+    matrix_s(0);
+    barrier();
+    vector(0);
+    commit(2);
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      fetch(t + 2);
+      matrix_full(t);
+      barrier();
+      vector(t);
+      commit(t + 2);
+      barrier();
     }
-    __syncthreads();
+    if (n_wave < n) {
+      fetch(n_wave + 2);
+      matrix_pv(n_wave);
+      barrier();
+      commit(n_wave + 2);
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        fetch(t + 2);
+        barrier();
+        commit(t + 2);
+        barrier();
+      }
+      barrier();
+      barrier();
+    } else {
+      matrix_pv(n);
+      barrier();
+      barrier();
+    }
+  } else {
+    fetch(2);
+    barrier();
+    matrix_s(0);
+    commit(2);
+    barrier();
+    fetch(3);
+    vector(0);
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      matrix_full(t);
+      commit(t + 2);
+      barrier();
+      fetch(t + 3);
+      vector(t);
+      barrier();
+    }
+    if (n_wave < n) {
+      matrix_pv(n_wave);
+      commit(n_wave + 2);
+      barrier();
+      fetch(n_wave + 3);
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        commit(t + 2);
+        barrier();
+        fetch(t + 3);
+        barrier();
+      }
+      barrier();
+    } else {
+      matrix_pv(n);
+      barrier();
+    }
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = (m_ref + log2 l) ln 2
-  const float l = l_part + swap_halves(l_part);
+  const float l = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   const float inv_l = 1.0f / l;
   if (q_lane < p.Sq) {
     bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
@@ -287,17 +436,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 // Software-exponential counts per lane per tile that are instantiated.
 constexpr int kEmuCounts[] = {0, 3, 8, 16, 32};
 
+template <int D, bool CAUSAL, int EMU>
+hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
+  auto kern = fwd_kernel<D, CAUSAL, EMU>;
+  const int lds = FwdLayout<D>::kLdsBytes;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, prm);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_d_causal(const FwdParams& prm, int emu, dim3 grid, hipStream_t stream) {
   switch (emu) {
-    case 0: hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0>), grid, dim3(kThreads), 0, stream, prm); break;
-    case 3: hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 3>), grid, dim3(kThreads), 0, stream, prm); break;
-    case 8: hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 8>), grid, dim3(kThreads), 0, stream, prm); break;
-    case 16: hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 16>), grid, dim3(kThreads), 0, stream, prm); break;
-    case 32: hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 32>), grid, dim3(kThreads), 0, stream, prm); break;
+    case 0: return launch_one<D, CAUSAL, 0>(prm, grid, stream);
+    case 3: return launch_one<D, CAUSAL, 3>(prm, grid, stream);
+    case 8: return launch_one<D, CAUSAL, 8>(prm, grid, stream);
+    case 16: return launch_one<D, CAUSAL, 16>(prm, grid, stream);
+    case 32: return launch_one<D, CAUSAL, 32>(prm, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
