@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // them (which would not fit the register budget of two waves per SIMD).
   constexpr int kNV = kKS * kDB;    // P V products
   constexpr int kNK = kKB * kKC;    // K Q^T products
-  auto matrix_stream = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
+  auto matrix_stream_body = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     constexpr bool SK = decltype(with_s)::value;
     constexpr int j0 = PV ? 0 : kNV;
@@ -251,6 +251,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // The matrix phase runs at raised wave priority so its MFMAs issue ahead of
+  // the vector-phase wave sharing the SIMD.
+  auto matrix_stream = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    matrix_stream_body(t, with_pv, with_s);
+    __builtin_amdgcn_s_setprio(0);
   };
   auto matrix_s = [&](int t) __attribute__((always_inline)) {
     matrix_stream(t, std::false_type{}, std::true_type{});
