@@ -1,71 +1,38 @@
 // Fused exact-attention backward for gfx950.
 //
-// Method.  The gradients of O = softmax(scale Q K^T) V, with P recomputed
-// from the forward's log-sum-exp, by five matrix products per tile (FA4 paper
-// §3.2.1, Eq. 7-8, as summarised on "FlashAttention-4: Algorithm and Kernel
-// Pipelining Co-Design for Asymmetric Hardware Scaling"):
+// Method.  The gradients of O = softmax(scale Q K^T) V with P recomputed from
+// the forward's log-sum-exp (FA4 paper §3.2 as summarised on "FlashAttention-4:
+// Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware Scaling"):
 //   S = Q K^T,  P = exp(scale S - LSE),  dP = dO V^T,  dS = P (dP - D),
-//   dV += P^T dO,  dK += scale dS^T Q,  dQ += scale dS K,
-// with D_i = sum_c dO_ic O_ic.  dQ is summed over key blocks in a float32
-// accumulator; the deterministic mode fixes the order of those additions with
-// a per-query-block turn counter (paper §1; the Korean summary of the paper,
-// §2.2, describes a lock that orders the dQ atomic adds).
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
+// with D_i = sum_c dO_ic O_ic.
 //
-// Kernels (one launch sequence per call, all on the caller's stream):
-//   bwd_prep     D_i, zeroed dQ accumulator, turn counters and work ticket;
-//   bwd_main     persistent workgroups take (key block, head) items from an
-//                atomic ticket; 4 wavefronts x 32 keys = 128 keys per item;
-//                query blocks of 64 rows are visited in DESCENDING order so
-//                that in the deterministic mode the items of one head meet
-//                each query block one after another (j = 0, 1, 2, ...) and
-//                waits stay short;
-//   bwd_dq_out   dQ = bf16(scale * accumulator).
-//
-// MFMA mapping (v_mfma_f32_32x32x16_bf16, lane layout in fa_device.hpp):
-//   S  = Q K^T    A = Q rows from LDS, B = the wave's K rows held in registers
-//   dP = dO V^T   A = dO rows from LDS, B = the wave's V rows in registers
-//     -> both accumulators hold one KEY per lane (16 query rows each);
-//   dV^T += dO^T P   B = P straight from the accumulator; A = dO^T staged
-//                    transposed in LDS in the accumulator's row order;
-//   dK^T += Q^T dS   likewise with Q^T;
-//   dQ  = dS K       dS goes through LDS (row-major, bf16); B = K^T staged
-//                    once per item in LDS; each wave owns 32 rows x d/2.
-//
-// Deadlock freedom of the deterministic mode: an item only waits for the
-// item of the same head with the next smaller key block, whose ticket is
-// smaller, so it was claimed earlier by a workgroup that is running or done;
-// by induction every wait ends.  Waits are also bounded: after a very long
-// spin the workgroup records an error flag and proceeds (the result is then
-// not reproducible, but the kernel terminates).
+// CDNA4 design (ours).  The paper adds every key block's dQ contribution with
+// atomics (and orders them behind a lock in its deterministic mode).  On
+// MI355X fp32 atomics to one accumulator from many XCDs run at ~1 TB/s, and
+// ordering them serialises the key blocks of a head.  Here the backward is
+// split by output instead, so every output element is written exactly once:
+//   bwd_prep_kernel   D_i;
+//   bwd_dq_kernel     a workgroup owns 256 query rows and streams K / V tiles:
+//                     S^T = K Q^T, dP^T = V dO^T (one query per lane, so LSE_i
+//                     and D_i are per-lane scalars), dS^T, dQ^T += K^T dS^T;
+//   bwd_dkdv_kernel   a workgroup owns 128 key rows and streams Q / dO tiles:
+//                     S = Q K^T, dP = dO V^T (one key per lane), P, dS,
+//                     dV^T += dO^T P, dK^T += Q^T dS.
+// That is seven products per tile pair instead of five, no atomics, no
+// workspace beyond D, and results that are bit-identical run to run in both
+// modes (the deterministic flag costs nothing).  Tiles use the layout of
+// fa_tiles.hpp, so Q, dO, K and V are each read both row-wise and transposed
+// from one LDS copy.
+
+#include <type_traits>
 
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBK = 128;   // keys per item (32 per wavefront)
-constexpr int kBQ = 64;    // query rows per step
-constexpr long long kSpinLimit = 1LL << 24;
-
-struct WorkspaceLayout {
-  size_t dqacc_off, dvec_off, turns_off, ctrl_off, total;
-};
-
-WorkspaceLayout workspace_layout(int B, int H, int Sq, int d) {
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  WorkspaceLayout w;
-  const size_t rows = (size_t)B * H * Sq;
-  const size_t n_qb = (size_t)B * H * ((Sq + kBQ - 1) / kBQ);
-  w.dqacc_off = 0;
-  w.dvec_off = up(rows * d * sizeof(float));
-  w.turns_off = w.dvec_off + up(rows * sizeof(float));
-  w.ctrl_off = w.turns_off + up(n_qb * sizeof(int));
-  w.total = w.ctrl_off + 256;   // [0] work ticket, [1] error flag
-  return w;
-}
 
 struct BwdParams {
   const bf16* q;
@@ -77,44 +44,16 @@ struct BwdParams {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* dqacc;
-  float* dvec;
-  int* turns;
-  int* ctrl;
+  float* dvec;   // D_i, [B, H, Sq]
   int BH, Sq, Sk;
-  int n_qb, n_kb, n_items;
   float scale;
   float scale_log2;
 };
 
+// ------------------------------------------------------------------- prep
 template <int D>
-struct BwdLayout {
-  static constexpr int kRowStride = D + 8;     // Q, dO row-major [q][d]
-  static constexpr int kTStride = kBQ + 8;     // Q^T, dO^T [d][q slot]
-  static constexpr int kSStride = kBK + 8;     // dS [q][key]
-  static constexpr int kKTStride = kBK + 8;    // K^T [d][key]
-  static constexpr int kQ = 0;
-  static constexpr int kDO = kQ + kBQ * kRowStride;
-  static constexpr int kQT = kDO + kBQ * kRowStride;
-  static constexpr int kDOT = kQT + D * kTStride;
-  static constexpr int kDS = kDOT + D * kTStride;
-  static constexpr int kKT = kDS + kBQ * kSStride;
-  static constexpr int kEnd = kKT + D * kKTStride;          // bf16 elements
-  static constexpr int kBytes = kEnd * 2 + 2 * kBQ * 4;     // + LSE*log2e, D
-  // staging units of a Q / dO block: 4 rows x 8 dims
-  static constexpr int kUnits = (kBQ / 4) * (D / 8);
-  static constexpr int kUnitsPerThread = (kUnits + kThreads - 1) / kThreads;
-  // staging units of the K^T block
-  static constexpr int kKUnits = (kBK / 4) * (D / 8);
-  static constexpr int kKUnitsPerThread = kKUnits / kThreads;
-  static_assert(kKUnits % kThreads == 0, "K^T staging must split evenly");
-};
-
-// ------------------------------------------------------------------ prep
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long rows, long long acc_vec4,
-                                                      int n_turns) {
-  // D_i = sum_c dO_ic O_ic: D/8 threads per row, 16 bytes each
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long rows) {
+  // D_i = sum_c dO_ic O_ic: D/8 lanes per row, 16 bytes each
   constexpr int kTPR = D / 8;
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
@@ -130,210 +69,401 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long ro
     for (int off = kTPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if ((t % kTPR) == 0) p.dvec[row] = s;
   }
-  f32x4* acc = reinterpret_cast<f32x4*>(p.dqacc);
-  for (long long t = gtid; t < acc_vec4; t += nthreads) acc[t] = f32x4{0, 0, 0, 0};
-  for (long long t = gtid; t < n_turns; t += nthreads) p.turns[t] = 0;
-  if (gtid < 64) p.ctrl[gtid] = 0;
 }
 
-// ------------------------------------------------------------- dQ out
+// ==================================================================== dQ
+// 8 wavefronts x 32 query rows; the two groups of four (one wave of each per
+// SIMD) alternate between a matrix phase and a vector phase as in the
+// forward kernel, one barrier per phase, raised priority in matrix phases.
+namespace dqk {
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kQW = 32;
+constexpr int kBM = kWaves * kQW;
+constexpr int kStages = 4;
+constexpr int kAhead = 4;
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_out_kernel(BwdParams p, long long n_vec4) {
-  const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long nthreads = (long long)gridDim.x * blockDim.x;
-  const f32x4* acc = reinterpret_cast<const f32x4*>(p.dqacc);
-  for (long long t = gtid; t < n_vec4; t += nthreads) {
-    const f32x4 a = acc[t] * p.scale;
-    *reinterpret_cast<bf16x4*>(p.dq + t * 4) = __builtin_convertvector(a, bf16x4);
-  }
-}
-
-// ------------------------------------------------------------- main
-template <int D>
-struct QBlockRegs {
-  u32x4 q[BwdLayout<D>::kUnitsPerThread][4];
-  u32x4 o[BwdLayout<D>::kUnitsPerThread][4];   // dO
-  float lse2;    // LSE * log2(e) of row tid (tid < kBQ)
-  float dval;    // D of row tid - kBQ (kBQ <= tid < 2 kBQ)
+struct Layout {
+  // keys per tile: 32 at d = 128 keeps a wave within 256 registers
+  static constexpr int kBN = D == 128 ? 32 : 64;
+  static constexpr int kTileBytes = kBN * TileGeom<D>::kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;   // K then V
+  static constexpr int kLdsBytes = kStages * kStageBytes;
 };
+}  // namespace dqk
 
-template <int D>
-__device__ __forceinline__ void load_qblock(QBlockRegs<D>& r, const BwdParams& p, int bh, int q0, int tid) {
-  using L = BwdLayout<D>;
-  const bf16* qh = p.q + (size_t)bh * p.Sq * D;
-  const bf16* oh = p.dout + (size_t)bh * p.Sq * D;
-#pragma unroll
-  for (int i = 0; i < L::kUnitsPerThread; ++i) {
-    const int u = tid + i * kThreads;
-    const int rq = u % (kBQ / 4);
-    const int dq = u / (kBQ / 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = q0 + 4 * rq + j;
-      const bool ok = (u < L::kUnits) && row < p.Sq;
-      r.q[i][j] = ok ? *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 8 * dq) : u32x4{0, 0, 0, 0};
-      r.o[i][j] = ok ? *reinterpret_cast<const u32x4*>(oh + (size_t)row * D + 8 * dq) : u32x4{0, 0, 0, 0};
-    }
-  }
-  if (tid < kBQ) {
-    const int row = q0 + tid;
-    // rows past the end get LSE = +inf, so their probabilities are exactly 0
-    r.lse2 = row < p.Sq ? p.lse[(size_t)bh * p.Sq + row] * kLog2e : __builtin_huge_valf();
-  } else if (tid < 2 * kBQ) {
-    const int row = q0 + tid - kBQ;
-    r.dval = row < p.Sq ? p.dvec[(size_t)bh * p.Sq + row] : 0.0f;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_qblock(const QBlockRegs<D>& r, bf16* smem, float* sf, int tid) {
-  using L = BwdLayout<D>;
-#pragma unroll
-  for (int i = 0; i < L::kUnitsPerThread; ++i) {
-    const int u = tid + i * kThreads;
-    if (u < L::kUnits) {
-      const int rq = u % (kBQ / 4);
-      const int dq = u / (kBQ / 4);
-      // row-major copies
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<u32x4*>(smem + L::kQ + (4 * rq + j) * L::kRowStride + 8 * dq) = r.q[i][j];
-        *reinterpret_cast<u32x4*>(smem + L::kDO + (4 * rq + j) * L::kRowStride + 8 * dq) = r.o[i][j];
-      }
-      // transposed copies, rows of each 16-row group in accumulator order
-      const int col = 16 * (rq / 4) + 4 * quad_slot(rq % 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        {
-          const uint32_t a = r.q[i][0][w], b = r.q[i][1][w], c = r.q[i][2][w], d = r.q[i][3][w];
-          *reinterpret_cast<u32x2*>(smem + L::kQT + (8 * dq + 2 * w) * L::kTStride + col) =
-              u32x2{lo_pair(a, b), lo_pair(c, d)};
-          *reinterpret_cast<u32x2*>(smem + L::kQT + (8 * dq + 2 * w + 1) * L::kTStride + col) =
-              u32x2{hi_pair(a, b), hi_pair(c, d)};
-        }
-        {
-          const uint32_t a = r.o[i][0][w], b = r.o[i][1][w], c = r.o[i][2][w], d = r.o[i][3][w];
-          *reinterpret_cast<u32x2*>(smem + L::kDOT + (8 * dq + 2 * w) * L::kTStride + col) =
-              u32x2{lo_pair(a, b), lo_pair(c, d)};
-          *reinterpret_cast<u32x2*>(smem + L::kDOT + (8 * dq + 2 * w + 1) * L::kTStride + col) =
-              u32x2{hi_pair(a, b), hi_pair(c, d)};
-        }
-      }
-    }
-  }
-  if (tid < kBQ) sf[tid] = r.lse2;
-  else if (tid < 2 * kBQ) sf[tid] = r.dval;
-}
-
-// K^T of the item's 128 keys into LDS, natural key order: kt[d][key].
-template <int D>
-__device__ __forceinline__ void stage_kt(const BwdParams& p, int bh, int k0, bf16* kt, int tid) {
-  using L = BwdLayout<D>;
-  const bf16* kh = p.k + (size_t)bh * p.Sk * D;
-#pragma unroll
-  for (int i = 0; i < L::kKUnitsPerThread; ++i) {
-    const int u = tid + i * kThreads;
-    const int kq = u % (kBK / 4);
-    const int dq = u / (kBK / 4);
-    u32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * kq + j;
-      r[j] = key < p.Sk ? *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + 8 * dq) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      *reinterpret_cast<u32x2*>(kt + (8 * dq + 2 * w) * L::kKTStride + 4 * kq) =
-          u32x2{lo_pair(r[0][w], r[1][w]), lo_pair(r[2][w], r[3][w])};
-      *reinterpret_cast<u32x2*>(kt + (8 * dq + 2 * w + 1) * L::kKTStride + 4 * kq) =
-          u32x2{hi_pair(r[0][w], r[1][w]), hi_pair(r[2][w], r[3][w])};
-    }
-  }
-}
-
-template <int D, bool CAUSAL, bool DET>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdParams p) {
-  using L = BwdLayout<D>;
-  constexpr int kKC = D / 16;       // 16-dim steps of S and dP
-  constexpr int kDB = D / 32;       // 32-dim blocks of dK^T / dV^T
-  constexpr int kQDB = D / 64;      // 32-dim blocks of one wave's dQ slice
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  float* sf = reinterpret_cast<float*>(smem + L::kEnd);   // [0,64) LSE*log2e, [64,128) D
-  __shared__ int s_item;
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  using namespace dqk;
+  using L = Layout<D>;
+  using G = TileGeom<D>;
+  constexpr int kBN = L::kBN;
+  constexpr int kKB = kBN / 32;   // 32-key blocks per tile
+  constexpr int kKS = kBN / 16;   // 16-key steps of K^T dS^T
+  constexpr int kDB = D / 32;     // 32-dim blocks of dQ^T
+  constexpr int kKC = D / 16;     // 16-dim steps of S^T and dP^T
+  constexpr int kNQ = kKS * kDB;  // dQ products per tile
+  constexpr int kNS = kKB * kKC;  // S^T (and as many dP^T) products per tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(&p.ctrl[0], 1);
-    __syncthreads();
-    const int item = s_item;
-    if (item >= p.n_items) break;
-    const int kb = item / p.BH;            // small key blocks (most work when causal) first
-    const int bh = item % p.BH;
-    const int k0 = kb * kBK;
-    const int key = k0 + wave * 32 + r32;  // this lane's key (B operand / accumulator column)
+  const int n_qblocks = (p.Sq + kBM - 1) / kBM;
+  const int rank = blockIdx.x / p.BH;
+  const int bh = blockIdx.x % p.BH;
+  const int qb = CAUSAL ? (n_qblocks - 1 - rank) : rank;
 
-    // the wave's K and V rows as B operands: lane holds row `key`, dims 16kc + 8g .. +8
-    bf16x8 kf[kKC], vf[kKC];
-    {
-      const bf16* kr = p.k + ((size_t)bh * p.Sk + key) * D + 8 * g;
-      const bf16* vr = p.v + ((size_t)bh * p.Sk + key) * D + 8 * g;
+  const unsigned head_q = (unsigned)p.Sq * G::kRowBytes;
+  const unsigned head_k = (unsigned)p.Sk * G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * D, head_q);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + (size_t)bh * p.Sq * D, head_q);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
+
+  const int q_wave_lo = qb * kBM + wave * kQW;
+  const int q_lane = q_wave_lo + r32;
+  const int row_lane = row_lane_offset<D>(lane);
+  const int tr_lane = tr_lane_offset<D>(lane);
+
+  // B operands: Q^T and dO^T of the lane's query, dims 16 kc + 8 g .. +8
+  bf16x8 qf[kKC], of[kKC];
 #pragma unroll
-      for (int kc = 0; kc < kKC; ++kc) {
-        kf[kc] = key < p.Sk ? *reinterpret_cast<const bf16x8*>(kr + kc * 16) : bf16x8{};
-        vf[kc] = key < p.Sk ? *reinterpret_cast<const bf16x8*>(vr + kc * 16) : bf16x8{};
+  for (int kc = 0; kc < kKC; ++kc) {
+    const unsigned off = (unsigned)q_lane * G::kRowBytes + (kc * 16 + 8 * g) * 2;
+    qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, off));
+    of[kc] = __builtin_bit_cast(bf16x8, load16(rdo, off));
+  }
+  const bool q_ok = q_lane < p.Sq;
+  const size_t qi = (size_t)bh * p.Sq + (q_ok ? q_lane : 0);
+  const float lse2 = q_ok ? p.lse[qi] * kLog2e : __builtin_huge_valf();   // rows past the end: P = 0
+  const float dval = q_ok ? p.dvec[qi] : 0.0f;
+
+  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM) : p.Sk;
+  const int n = (kv_end + kBN - 1) / kBN;
+  const int n_wave = CAUSAL ? min(n, (q_wave_lo + kQW - 1) / kBN + 1) : n;
+
+  f32x16 dq[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) dq[db] = f32x16{};
+  f32x16 s[kKB], dp[kKB];
+  bf16x8 pk[kKS];   // dS^T in bf16: B operands of K^T dS^T
+
+  // ---- matrix phase: dQ^T += K_{t-1}^T dS_{t-1}^T, then S_t^T = K_t Q^T and
+  // dP_t^T = V_t dO^T; one stream of MFMAs whose LDS operands are read
+  // kAhead ahead through a register ring.
+  auto matrix_body = [&](int t, auto with_dq, auto with_s) __attribute__((always_inline)) {
+    constexpr bool DQ = decltype(with_dq)::value;
+    constexpr bool SP = decltype(with_s)::value;
+    constexpr int j0 = DQ ? 0 : kNQ;
+    constexpr int j1 = SP ? kNQ + 2 * kNS : kNQ;
+    const char* kprev = smem + ((t + kStages - 1) % kStages) * L::kStageBytes;
+    const char* kcur = smem + (t % kStages) * L::kStageBytes;
+    const char* vcur = kcur + L::kTileBytes;
+    // j < kNQ: (ks, db) = (j / kDB, j % kDB); then pairs (S, dP) for (kc, kb)
+    auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+      if (j < kNQ) return read_cols<D>(kprev, tr_lane, j / kDB, j % kDB);
+      const int i = (j - kNQ) >> 1;
+      const int kb = i % kKB, kc = i / kKB;
+      return ((j - kNQ) & 1) ? read_rows<D>(vcur, row_lane, kb, kc) : read_rows<D>(kcur, row_lane, kb, kc);
+    };
+    if (SP) {
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
       }
     }
-    stage_kt<D>(p, bh, k0, smem + L::kKT, tid);
-
-    f32x16 dk[kDB], dv[kDB];
+    bf16x8 ring[kAhead];
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      dk[db] = f32x16{};
-      dv[db] = f32x16{};
+    for (int j = j0; j < j0 + kAhead && j < j1; ++j) ring[(j - j0) % kAhead] = operand(j);
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const bf16x8 a = ring[(j - j0) % kAhead];
+      if (j + kAhead < j1) ring[(j - j0) % kAhead] = operand(j + kAhead);
+      if (j < kNQ) {
+        dq[j % kDB] = mfma32x32x16(a, pk[j / kDB], dq[j % kDB]);
+      } else {
+        const int i = (j - kNQ) >> 1;
+        const int kb = i % kKB, kc = i / kKB;
+        if ((j - kNQ) & 1) dp[kb] = mfma32x32x16(a, of[kc], dp[kb]);
+        else s[kb] = mfma32x32x16(a, qf[kc], s[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto matrix = [&](int t, auto with_dq, auto with_s) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    matrix_body(t, with_dq, with_s);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    // query blocks that see at least one of these keys, visited top down
-    const int qb_lo = CAUSAL ? k0 / kBQ : 0;
-    const int qb_hi = p.n_qb - 1;
-    QBlockRegs<D> regs;
-    if (qb_lo <= qb_hi) load_qblock<D>(regs, p, bh, qb_hi * kBQ, tid);
-    __syncthreads();   // previous item done with LDS
-    if (qb_lo <= qb_hi) store_qblock<D>(regs, smem, sf, tid);
-    __syncthreads();
+  // ---- vector phase: P^T and dS^T of tile t, packed to bf16
+  auto vector = [&](int t) __attribute__((always_inline)) {
+    if (t >= n_wave) return;
+    const int k0 = t * kBN;
+    const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = exp2_hw(__builtin_fmaf(s[kb][i], p.scale_log2, -lse2));
+        if (need_mask) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= p.Sk || (CAUSAL && key > q_lane)) pv = 0.0f;
+        }
+        s[kb][i] = pv * (dp[kb][i] - dval);
+      }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const int kb = ks >> 1, h = (ks & 1) * 8;
+      pk[ks] = pack_bf16x8(s[kb][h], s[kb][h + 1], s[kb][h + 2], s[kb][h + 3], s[kb][h + 4], s[kb][h + 5],
+                           s[kb][h + 6], s[kb][h + 7]);
+    }
+  };
 
-    for (int qb = qb_hi; qb >= qb_lo; --qb) {
-      const int q0 = qb * kBQ;
-      const bool has_next = qb - 1 >= qb_lo;
-      if (has_next) load_qblock<D>(regs, p, bh, q0 - kBQ, tid);
+  TileIO<D, kBN, kWaves> kio, vio;
+  auto fetch = [&](int u) __attribute__((always_inline)) {
+    if (u < n) {
+      kio.fetch(rk, u * kBN, wave, lane);
+      vio.fetch(rv, u * kBN, wave, lane);
+    }
+  };
+  auto commit = [&](int u) __attribute__((always_inline)) {
+    if (u < n) {
+      char* st = smem + (u % kStages) * L::kStageBytes;
+      kio.store(st, wave, lane);
+      vio.store(st + L::kTileBytes, wave, lane);
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto m_s = [&](int t) __attribute__((always_inline)) { matrix(t, std::false_type{}, std::true_type{}); };
+  auto m_full = [&](int t) __attribute__((always_inline)) { matrix(t, std::true_type{}, std::true_type{}); };
+  auto m_dq = [&](int t) __attribute__((always_inline)) { matrix(t, std::true_type{}, std::false_type{}); };
 
-      // ---- S = Q K^T and dP = dO V^T: 2 blocks of 32 query rows
+  fetch(0);
+  commit(0);
+  fetch(1);
+  commit(1);
+  barrier();
+
+  // Same interval schedule as the forward kernel: group 0 runs matrix(t) in
+  // interval 2t+1 and vector(t) in 2t+2; group 1 is one interval behind;
+  // tile u is fetched in interval 2u-3 and written at the end of 2u-2.
+  if (group == 0) {
+    fetch(2);
+    m_s(0);
+    barrier();
+    vector(0);
+    commit(2);
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      fetch(t + 2);
+      m_full(t);
+      barrier();
+      vector(t);
+      commit(t + 2);
+      barrier();
+    }
+    if (n_wave < n) {
+      fetch(n_wave + 2);
+      m_dq(n_wave);
+      barrier();
+      commit(n_wave + 2);
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        fetch(t + 2);
+        barrier();
+        commit(t + 2);
+        barrier();
+      }
+      barrier();
+      barrier();
+    } else {
+      m_dq(n);
+      barrier();
+      barrier();
+    }
+  } else {
+    fetch(2);
+    barrier();
+    m_s(0);
+    commit(2);
+    barrier();
+    fetch(3);
+    vector(0);
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      m_full(t);
+      commit(t + 2);
+      barrier();
+      fetch(t + 3);
+      vector(t);
+      barrier();
+    }
+    if (n_wave < n) {
+      m_dq(n_wave);
+      commit(n_wave + 2);
+      barrier();
+      fetch(n_wave + 3);
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        commit(t + 2);
+        barrier();
+        fetch(t + 3);
+        barrier();
+      }
+      barrier();
+    } else {
+      m_dq(n);
+      barrier();
+    }
+  }
+
+  // ---- dQ = scale (dQ^T)^T -> bf16 (lane = query, 4 consecutive dims per group)
+  if (q_ok) {
+    bf16* row = p.dq + qi * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v4 = {dq[db][4 * i4] * p.scale, dq[db][4 * i4 + 1] * p.scale, dq[db][4 * i4 + 2] * p.scale,
+                          dq[db][4 * i4 + 3] * p.scale};
+        *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+}
+
+// =================================================================== dK dV
+// 4 wavefronts x 32 keys = 128 keys per workgroup; query tiles of 64 rows in
+// a 2-stage LDS ring (register prefetch, one barrier per tile).
+namespace kvk {
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kKW = 32;
+constexpr int kBK = kWaves * kKW;
+constexpr int kBQ = 64;
+constexpr int kStages = 2;
+template <int D>
+struct Layout {
+  static constexpr int kTileBytes = kBQ * TileGeom<D>::kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kBQ * 4;   // Q, dO, LSE*log2e, D
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+};
+}  // namespace kvk
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using namespace kvk;
+  using L = Layout<D>;
+  using G = TileGeom<D>;
+  constexpr int kKC = D / 16;   // 16-dim steps of S and dP
+  constexpr int kDB = D / 32;   // 32-dim blocks of dK^T / dV^T
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int kb = blockIdx.x / p.BH;   // small key blocks (most work when causal) first
+  const int bh = blockIdx.x % p.BH;
+  const int k0 = kb * kBK;
+  const int k_wave_lo = k0 + wave * kKW;
+  const int key = k_wave_lo + r32;
+
+  const unsigned head_q = (unsigned)p.Sq * G::kRowBytes;
+  const unsigned head_k = (unsigned)p.Sk * G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * D, head_q);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + (size_t)bh * p.Sq * D, head_q);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
+
+  const int row_lane = row_lane_offset<D>(lane);
+  const int tr_lane = tr_lane_offset<D>(lane);
+
+  // B operands: the lane's K and V rows, dims 16 kc + 8 g .. +8
+  bf16x8 kf[kKC], vf[kKC];
+#pragma unroll
+  for (int kc = 0; kc < kKC; ++kc) {
+    const unsigned off = (unsigned)key * G::kRowBytes + (kc * 16 + 8 * g) * 2;
+    kf[kc] = __builtin_bit_cast(bf16x8, load16(rk, off));
+    vf[kc] = __builtin_bit_cast(bf16x8, load16(rv, off));
+  }
+
+  f32x16 dk[kDB], dv[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int n_qt = (p.Sq + kBQ - 1) / kBQ;
+  const int qt_lo = CAUSAL ? k0 / kBQ : 0;
+
+  TileIO<D, kBQ, kWaves> qio, oio;
+  float rowval = 0.0f;   // tid < kBQ: LSE*log2e of a row; kBQ <= tid < 2 kBQ: D of a row
+  auto fetch = [&](int qt) __attribute__((always_inline)) {
+    qio.fetch(rq, qt * kBQ, wave, lane);
+    oio.fetch(rdo, qt * kBQ, wave, lane);
+    const int r = qt * kBQ + (tid & (kBQ - 1));
+    const bool ok = r < p.Sq;
+    const size_t ri = (size_t)bh * p.Sq + (ok ? r : 0);
+    if (tid < kBQ) rowval = ok ? p.lse[ri] * kLog2e : __builtin_huge_valf();   // past the end: P = 0
+    else if (tid < 2 * kBQ) rowval = ok ? p.dvec[ri] : 0.0f;
+  };
+  auto commit = [&](int stage) __attribute__((always_inline)) {
+    char* st = smem + stage * L::kStageBytes;
+    qio.store(st, wave, lane);
+    oio.store(st + L::kTileBytes, wave, lane);
+    if (tid < 2 * kBQ) reinterpret_cast<float*>(st + 2 * L::kTileBytes)[tid] = rowval;
+  };
+
+  if (qt_lo < n_qt) {
+    fetch(qt_lo);
+    commit(0);
+  }
+  lds_barrier();
+
+  for (int qt = qt_lo; qt < n_qt; ++qt) {
+    const int stage = (qt - qt_lo) & 1;
+    const char* qtile = smem + stage * L::kStageBytes;
+    const char* otile = qtile + L::kTileBytes;
+    const float* rows = reinterpret_cast<const float*>(qtile + 2 * L::kTileBytes);
+    const bool has_next = qt + 1 < n_qt;
+    if (has_next) fetch(qt + 1);
+    const int q0 = qt * kBQ;
+    // causal: skip tiles whose rows all precede the wave's keys
+    if (!CAUSAL || k_wave_lo <= q0 + kBQ - 1) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         s[b] = f32x16{};
         dp[b] = f32x16{};
-        const bf16* qrow = smem + L::kQ + (b * 32 + r32) * L::kRowStride + 8 * g;
-        const bf16* orow = smem + L::kDO + (b * 32 + r32) * L::kRowStride + 8 * g;
 #pragma unroll
         for (int kc = 0; kc < kKC; ++kc) {
-          s[b] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(qrow + kc * 16), kf[kc], s[b]);
-          dp[b] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(orow + kc * 16), vf[kc], dp[b]);
+          s[b] = mfma32x32x16(read_rows<D>(qtile, row_lane, b, kc), kf[kc], s[b]);
+          dp[b] = mfma32x32x16(read_rows<D>(otile, row_lane, b, kc), vf[kc], dp[b]);
         }
       }
-      // ---- P and dS (lane = key, 16 query rows per block)
-      const bool need_mask = (CAUSAL && q0 < k0 + kBK - 1) || key >= p.Sk;
+      // P and dS (lane = key, 16 query rows per block)
+      const bool need_mask = (CAUSAL && k_wave_lo + kKW - 1 > q0) || (k0 + kBK > p.Sk);
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = b * 32 + 8 * i4 + 4 * g;   // first of 4 consecutive rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sf + r0);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sf + kBQ + r0);
+          const int r0 = b * 32 + 8 * i4 + 4 * g;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rows + r0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rows + kBQ + r0);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 4 * i4 + j;
@@ -343,16 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdParams p) {
             dp[b][i] = pv * (dp[b][i] - d4[j]);
           }
         }
-      // ---- dS -> LDS (bf16, row-major [q][key]) for the dQ product
-      {
-        bf16* dsb = smem + L::kDS + wave * 32 + r32;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            dsb[(b * 32 + 8 * (i >> 2) + 4 * g + (i & 3)) * L::kSStride] = (bf16)dp[b][i];
-      }
-      // ---- dV^T += dO^T P,  dK^T += Q^T dS
+      // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
       for (int ks = 0; ks < kBQ / 16; ++ks) {
         const int b = ks >> 1, h = (ks & 1) * 8;
@@ -362,134 +483,65 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdParams p) {
                                       dp[b][h + 5], dp[b][h + 6], dp[b][h + 7]);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          const int off = (db * 32 + r32) * L::kTStride + ks * 16 + 8 * g;
-          dv[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(smem + L::kDOT + off), bp, dv[db]);
-          dk[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(smem + L::kQT + off), bs, dk[db]);
+          dv[db] = mfma32x32x16(read_cols<D>(otile, tr_lane, ks, db), bp, dv[db]);
+          dk[db] = mfma32x32x16(read_cols<D>(qtile, tr_lane, ks, db), bs, dk[db]);
         }
       }
-      __syncthreads();   // dS complete
-
-      // ---- dQ slice of this wave: rows 32 (wave / 2) .. +32, dims (wave % 2) D/2 .. +D/2
-      f32x16 dqp[kQDB];
-      {
-        const int qr = (wave >> 1) * 32;
-        const int dc = (wave & 1) * (D / 2);
-        const bf16* arow = smem + L::kDS + (qr + r32) * L::kSStride + 8 * g;
-#pragma unroll
-        for (int db = 0; db < kQDB; ++db) {
-          dqp[db] = f32x16{};
-          const bf16* brow = smem + L::kKT + (dc + db * 32 + r32) * L::kKTStride + 8 * g;
-#pragma unroll
-          for (int ks = 0; ks < kBK / 16; ++ks)
-            dqp[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + ks * 16),
-                                   *reinterpret_cast<const bf16x8*>(brow + ks * 16), dqp[db]);
-        }
-      }
-      int* turn = p.turns + (size_t)bh * p.n_qb + qb;
-      if (DET) {
-        if (tid == 0) {
-          long long spins = 0;
-          while (__hip_atomic_load(turn, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != kb) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
-              __hip_atomic_store(&p.ctrl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-          }
-        }
-        __syncthreads();
-      }
-      {
-        const int qr = (wave >> 1) * 32;
-        const int dc = (wave & 1) * (D / 2);
-        float* accb = p.dqacc + ((size_t)bh * p.Sq + q0 + qr) * D + dc + r32;
-#pragma unroll
-        for (int db = 0; db < kQDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 8 * (i >> 2) + 4 * g + (i & 3);
-            if (q0 + qr + row < p.Sq) unsafeAtomicAdd(accb + (size_t)row * D + db * 32, dqp[db][i]);
-          }
-      }
-      if (DET) {
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(turn, kb + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();   // all LDS reads of this block done
-      if (has_next) store_qblock<D>(regs, smem, sf, tid);
-      __syncthreads();
     }
+    if (has_next) commit(stage ^ 1);
+    lds_barrier();
+  }
 
-    // ---- dK = scale dK^T^T, dV = dV^T^T (lane = key; 4 consecutive dims per group)
-    if (key < p.Sk) {
-      bf16* dkr = p.dk + ((size_t)bh * p.Sk + key) * D;
-      bf16* dvr = p.dv + ((size_t)bh * p.Sk + key) * D;
+  // ---- dK = scale (dK^T)^T, dV = (dV^T)^T -> bf16 (lane = key)
+  if (key < p.Sk) {
+    bf16* dkr = p.dk + ((size_t)bh * p.Sk + key) * D;
+    bf16* dvr = p.dv + ((size_t)bh * p.Sk + key) * D;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int c = db * 32 + 8 * i4 + 4 * g;
-          const f32x4 a = {dk[db][4 * i4] * p.scale, dk[db][4 * i4 + 1] * p.scale, dk[db][4 * i4 + 2] * p.scale,
-                           dk[db][4 * i4 + 3] * p.scale};
-          const f32x4 b = {dv[db][4 * i4], dv[db][4 * i4 + 1], dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]};
-          *reinterpret_cast<bf16x4*>(dkr + c) = __builtin_convertvector(a, bf16x4);
-          *reinterpret_cast<bf16x4*>(dvr + c) = __builtin_convertvector(b, bf16x4);
-        }
-    }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int c = db * 32 + 8 * i4 + 4 * g;
+        const f32x4 a = {dk[db][4 * i4] * p.scale, dk[db][4 * i4 + 1] * p.scale, dk[db][4 * i4 + 2] * p.scale,
+                         dk[db][4 * i4 + 3] * p.scale};
+        const f32x4 b = {dv[db][4 * i4], dv[db][4 * i4 + 1], dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]};
+        *reinterpret_cast<bf16x4*>(dkr + c) = __builtin_convertvector(a, bf16x4);
+        *reinterpret_cast<bf16x4*>(dvr + c) = __builtin_convertvector(b, bf16x4);
+      }
   }
 }
 
-template <int D, bool CAUSAL, bool DET>
-hipError_t launch_main(const BwdParams& prm, hipStream_t stream, int n_cu) {
-  using L = BwdLayout<D>;
-  const int per_cu = (160 * 1024) / L::kBytes >= 2 ? 2 : 1;
-  int grid = n_cu * per_cu;
-  if (grid > prm.n_items) grid = prm.n_items;
-  auto kern = bwd_main_kernel<D, CAUSAL, DET>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::kBytes);
+template <typename K>
+hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int lds, hipStream_t stream, const BwdParams& prm) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), L::kBytes, stream, prm);
+  hipLaunchKernelGGL(kern, grid, block, lds, stream, prm);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_all(const BwdArgs& a, BwdParams& prm, hipStream_t stream) {
-  const WorkspaceLayout w = workspace_layout(a.B, a.H, a.Sq, D);
-  char* ws = static_cast<char*>(a.workspace);
-  prm.dqacc = reinterpret_cast<float*>(ws + w.dqacc_off);
-  prm.dvec = reinterpret_cast<float*>(ws + w.dvec_off);
-  prm.turns = reinterpret_cast<int*>(ws + w.turns_off);
-  prm.ctrl = reinterpret_cast<int*>(ws + w.ctrl_off);
+  prm.dvec = static_cast<float*>(a.workspace);
   const long long rows = (long long)a.B * a.H * a.Sq;
-  const long long acc_vec4 = rows * D / 4;
-  const int n_turns = prm.BH * prm.n_qb;
-
-  int dev = 0, n_cu = 256;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(1024), dim3(256), 0, stream, prm, rows);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(2048), dim3(256), 0, stream, prm, rows, acc_vec4, n_turns);
-  e = hipGetLastError();
+  const dim3 gq((unsigned)(((a.Sq + dqk::kBM - 1) / dqk::kBM) * prm.BH));
+  e = a.causal ? launch_dyn(bwd_dq_kernel<D, true>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm)
+               : launch_dyn(bwd_dq_kernel<D, false>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm);
   if (e != hipSuccess) return e;
-  if (a.causal) {
-    e = a.deterministic ? launch_main<D, true, true>(prm, stream, n_cu) : launch_main<D, true, false>(prm, stream, n_cu);
-  } else {
-    e = a.deterministic ? launch_main<D, false, true>(prm, stream, n_cu)
-                        : launch_main<D, false, false>(prm, stream, n_cu);
-  }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_out_kernel<D>, dim3(2048), dim3(256), 0, stream, prm, acc_vec4);
-  return hipGetLastError();
+
+  const dim3 gk((unsigned)(((a.Sk + kvk::kBK - 1) / kvk::kBK) * prm.BH));
+  return a.causal
+             ? launch_dyn(bwd_dkdv_kernel<D, true>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm)
+             : launch_dyn(bwd_dkdv_kernel<D, false>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm);
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int d, bool /*deterministic*/) {
-  return workspace_layout(B, H, Sq, d).total;
+size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int /*d*/, bool /*deterministic*/) {
+  return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~size_t(255);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -506,9 +558,6 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   prm.BH = a.B * a.H;
   prm.Sq = a.Sq;
   prm.Sk = a.Sk;
-  prm.n_qb = (a.Sq + kBQ - 1) / kBQ;
-  prm.n_kb = (a.Sk + kBK - 1) / kBK;
-  prm.n_items = prm.n_kb * prm.BH;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale * kLog2e;
   return a.d == 64 ? launch_all<64>(a, prm, stream) : launch_all<128>(a, prm, stream);

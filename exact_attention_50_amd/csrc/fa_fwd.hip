@@ -26,15 +26,16 @@
 //   * O^T = V^T P^T: the S^T accumulator, rounded to bf16, is already the B
 //     operand (keys of each 16-key group in a fixed permuted order); the V^T
 //     A operand is read from row-major V in LDS with ds_read_b64_tr_b16;
-//   * K / V tiles: 4-stage LDS ring, XOR-swizzled at 16-byte granularity so
-//     the MFMA operand reads are bank-conflict free; each tile is fetched to
-//     registers one matrix phase ahead and written to LDS one phase later;
+//   * K / V tiles: 4-stage LDS ring with the chunk permutation of
+//     fa_tiles.hpp (bank-conflict-free operand reads); each tile is fetched
+//     to registers one matrix phase ahead and written to LDS one phase later;
 //     buffer descriptors bound every head, so rows past the end read zeros.
 
 #include <type_traits>
 
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
 namespace {
@@ -62,104 +63,12 @@ struct FwdParams {
 template <int D>
 struct FwdLayout {
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
   static constexpr int kTileBytes = kBN * kRowBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kRowsPerLoad = 64 / kChunks;        // rows of one wave-wide 16-byte load
-  static constexpr int kLoadsPerWave = kBN / kRowsPerLoad / kWaves;
-  static_assert(kLoadsPerWave >= 1, "tile too small for the workgroup");
 };
 
-// 16-byte chunk position of chunk c of row r (bank-conflict-free reads: K by
-// 32 rows at one chunk, V by ds_read_b64_tr_b16 over 4 rows x 4 chunks).
-template <int D>
-__device__ __forceinline__ int k_pos(int r, int c) {
-  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-}
-template <int D>
-__device__ __forceinline__ int v_pos(int r, int c) {
-  return D == 128 ? (c ^ ((r & 3) << 2)) : (c ^ (((r >> 1) & 1) << 2));
-}
-
-template <int D>
-struct TileRegs {
-  u32x4 k[FwdLayout<D>::kLoadsPerWave];
-  u32x4 v[FwdLayout<D>::kLoadsPerWave];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int k0, int wave, int lane) {
-  using L = FwdLayout<D>;
-#pragma unroll
-  for (int i = 0; i < L::kLoadsPerWave; ++i) {
-    const int row = (i * kWaves + wave) * L::kRowsPerLoad + lane / L::kChunks;
-    const unsigned off = (unsigned)(k0 + row) * L::kRowBytes + (lane % L::kChunks) * 16;
-    r.k[i] = load16(rk, off);
-    r.v[i] = load16(rv, off);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* stage, int wave, int lane) {
-  using L = FwdLayout<D>;
-#pragma unroll
-  for (int i = 0; i < L::kLoadsPerWave; ++i) {
-    const int row = (i * kWaves + wave) * L::kRowsPerLoad + lane / L::kChunks;
-    const int c = lane % L::kChunks;
-    *reinterpret_cast<u32x4*>(stage + row * L::kRowBytes + k_pos<D>(row, c) * 16) = r.k[i];
-    *reinterpret_cast<u32x4*>(stage + L::kTileBytes + row * L::kRowBytes + v_pos<D>(row, c) * 16) = r.v[i];
-  }
-}
-
-constexpr int kAhead = 6;   // MFMA operands in flight per wave
-
-// LDS operand addressing.  With the XOR swizzles above, the byte offset of
-// every MFMA operand read factors into a per-lane base XOR a small constant
-// plus a constant, so each read needs one base register and an immediate:
-//
-//  K (A operand of S^T = K Q^T; rows 32 kb + r, dims 16 kc + 8 g .. +8):
-//    off = (k_lane ^ 32 kc) + 32 kb * RowBytes
-//    with k_lane = r RowBytes + 32 (x >> 1) + 16 (g ^ (x & 1)), x the row's
-//    swizzle key (r & 15 for d = 128, (r >> 1) & 7 for d = 64);
-//  V^T (A operand of O^T = V^T P^T; dims 32 db .. +32, keys of step ks, read
-//  as two ds_read_b64_tr_b16 of 4 keys x 16 dims, half jh):
-//    off = (v_lane ^ 64 db) + (16 ks + 8 jh) RowBytes
-//    with s = lane % 16, w the swizzle bit(s) of the lane's key
-//    ((s >> 2) & 3 for d = 128, (s >> 3) & 1 for d = 64),
-//    v_lane = (4 g + (s >> 2)) RowBytes + 64 w + 16 (2 ((lane >> 4) & 1)
-//             + ((s & 3) >> 1)) + 8 (s & 1).
-// The 16 keys of step ks arrive in the accumulator's order: slot 8 g + j
-// holds key 8 (j / 4) + 4 g + j % 4.
-template <int D>
-__device__ __forceinline__ int k_lane_offset(int lane) {
-  using L = FwdLayout<D>;
-  const int r = lane & 31, g = lane >> 5;
-  const int x = D == 128 ? (r & 15) : ((r >> 1) & 7);
-  return r * L::kRowBytes + 32 * (x >> 1) + 16 * (g ^ (x & 1));
-}
-template <int D>
-__device__ __forceinline__ int v_lane_offset(int lane) {
-  using L = FwdLayout<D>;
-  const int s16 = lane & 15, g = lane >> 5;
-  const int w = D == 128 ? ((s16 >> 2) & 3) : ((s16 >> 3) & 1);
-  return (4 * g + (s16 >> 2)) * L::kRowBytes + 64 * w + 16 * (2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1)) +
-         8 * (s16 & 1);
-}
-template <int D>
-__device__ __forceinline__ bf16x8 read_k(const char* kst, int k_lane, int kb, int kc) {
-  using L = FwdLayout<D>;
-  return *reinterpret_cast<const bf16x8*>(kst + (k_lane ^ (32 * kc)) + 32 * kb * L::kRowBytes);
-}
-template <int D>
-__device__ __forceinline__ bf16x8 read_vt(const char* vst, int v_lane, int ks, int db) {
-  using L = FwdLayout<D>;
-  const char* base = vst + (v_lane ^ (64 * db)) + 16 * ks * L::kRowBytes;
-  const bf16x4_t lo = lds_read_tr16(base);
-  const bf16x4_t hi = lds_read_tr16(base + 8 * L::kRowBytes);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
+constexpr int kAhead = 6;   // MFMA operand fragments in flight per wave
 
 template <int D, bool CAUSAL, int EMU>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
@@ -191,8 +100,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
   const int q_wave_lo = qb * kBM + wave * kQW;
   const int q_lane = q_wave_lo + r32;
-  const int k_lane = k_lane_offset<D>(lane);
-  const int v_lane = v_lane_offset<D>(lane);
+  const int k_lane = row_lane_offset<D>(lane);
+  const int v_lane = tr_lane_offset<D>(lane);
 
   // Q^T operand: lane holds Q[q_lane][16 kc + 8 g .. +8] (zeros past the end)
   bf16x8 qf[kKC];
@@ -228,9 +137,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const char* kst = smem + (t % kStages) * L::kStageBytes;
     // j < kNV: (ks, db) = (j / kDB, j % kDB); j >= kNV: (kc, kb) = (i / kKB, i % kKB), i = j - kNV
     auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-      if (j < kNV) return read_vt<D>(vst, v_lane, j / kDB, j % kDB);
+      if (j < kNV) return read_cols<D>(vst, v_lane, j / kDB, j % kDB);
       const int i = j - kNV;
-      return read_k<D>(kst, k_lane, i % kKB, i / kKB);
+      return read_rows<D>(kst, k_lane, i % kKB, i / kKB);
     };
     if (SK) {
 #pragma unroll
@@ -324,12 +233,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
-  TileRegs<D> regs;
+  TileIO<D, kBN, kWaves> kio, vio;
   auto fetch = [&](int u) __attribute__((always_inline)) {
-    if (u < n) load_tile<D>(regs, rk, rv, u * kBN, wave, lane);
+    if (u < n) {
+      kio.fetch(rk, u * kBN, wave, lane);
+      vio.fetch(rv, u * kBN, wave, lane);
+    }
   };
   auto commit = [&](int u) __attribute__((always_inline)) {
-    if (u < n) store_tile<D>(regs, smem + (u % kStages) * L::kStageBytes, wave, lane);
+    if (u < n) {
+      char* st = smem + (u % kStages) * L::kStageBytes;
+      kio.store(st, wave, lane);
+      vio.store(st + L::kTileBytes, wave, lane);
+    }
   };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);

@@ -1,0 +1,103 @@
+// LDS tiles of bf16 rows shared by the attention kernels (gfx950).
+//
+// A tile holds ROWS consecutive rows of a [S, D] bf16 tensor, row r at byte
+// r * 2D.  Its 16-byte chunks are permuted inside each row,
+//     chunk c of row r lives at chunk position c ^ f(r),
+// with f(r) = 4 (r & 3) + ((r >> 2) & 3)          for D = 128 (16 chunks/row),
+//      f(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)   for D = 64  (8 chunks/row),
+// which makes both ways the kernels read a tile free of LDS bank conflicts:
+//   * row reads (MFMA A operand with rows = tile rows, k = D): 32 rows at one
+//     chunk, 16 bytes per lane (ds_read_b128);
+//   * transposed reads (A operand with rows = D, k = tile rows): 4 rows x 4
+//     chunks per 32 lanes, 8 bytes per lane (ds_read_b64_tr_b16).
+// The same tile can therefore serve as K and as K^T, V and V^T, Q and Q^T.
+//
+// Addressing.  With this permutation every operand read is a per-lane base
+// XOR a small constant plus a constant (an immediate of the LDS instruction):
+//   row read, rows 32 kb + r, dims 16 kc + 8 g .. +8:
+//       (row_lane ^ 32 kc) + 32 kb * RowBytes
+//   transposed read, dims 32 db .. +32, rows 16 ks + 8 jh + (4 g + s / 4),
+//   s = lane % 16:
+//       ((tr_lane ^ 32 jh) ^ 64 db) + (16 ks + 8 jh) RowBytes
+// and the 16 rows of step ks arrive in the MFMA accumulator's row order (slot
+// 8 g + j holds row 8 (j / 4) + 4 g + j % 4), so an accumulator rounded to
+// bf16 is directly the matching B operand.
+#pragma once
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+template <int D>
+struct TileGeom {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 64 / kChunks;   // rows of one wave-wide 16-byte load
+};
+
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+}
+
+template <int D>
+__device__ __forceinline__ int row_lane_offset(int lane) {
+  const int r = lane & 31, g = lane >> 5;
+  const int x = tile_swz<D>(r);
+  return r * TileGeom<D>::kRowBytes + 32 * (x >> 1) + 16 * (g ^ (x & 1));
+}
+
+template <int D>
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int s16 = lane & 15, g = lane >> 5;
+  const int w = D == 128 ? ((s16 >> 2) & 3) : ((s16 >> 3) & 1);
+  const int part = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+  return (4 * g + (s16 >> 2)) * TileGeom<D>::kRowBytes + 64 * w + 16 * (part ^ g) + 8 * (s16 & 1);
+}
+
+// A operand, rows 32 kb .. +32 of the tile, dims 16 kc + 8 g .. +8.
+template <int D>
+__device__ __forceinline__ bf16x8 read_rows(const char* tile, int row_lane, int kb, int kc) {
+  return *reinterpret_cast<const bf16x8*>(tile + (row_lane ^ (32 * kc)) + 32 * kb * TileGeom<D>::kRowBytes);
+}
+
+// A operand with rows = dims 32 db .. +32 and k = the 16 tile rows of step ks,
+// in accumulator row order (two ds_read_b64_tr_b16 of 4 rows x 16 dims).
+template <int D>
+__device__ __forceinline__ bf16x8 read_cols(const char* tile, int tr_lane, int ks, int db) {
+  constexpr int RB = TileGeom<D>::kRowBytes;
+  const bf16x4_t lo = lds_read_tr16(tile + (tr_lane ^ (64 * db)) + 16 * ks * RB);
+  const bf16x4_t hi = lds_read_tr16(tile + ((tr_lane ^ 32) ^ (64 * db)) + (16 * ks + 8) * RB);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Wave-wide bounds-checked fetch of a tile's share into registers and its
+// store into LDS with the chunk permutation.  ROWS rows are split over NW
+// waves; wave `wave` handles loads i = 0 .. kLoads-1 (rows of load (i NW +
+// wave)).  Rows at or past the descriptor's end read as zeros.
+template <int D, int ROWS, int NW>
+struct TileIO {
+  static constexpr int kLoads = ROWS / TileGeom<D>::kRowsPerLoad / NW;
+  static_assert(kLoads >= 1, "tile too small for the workgroup");
+  u32x4 r[kLoads];
+
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane) {
+    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
+      r[i] = load16(src, (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + (lane % TileGeom<D>::kChunks) * 16);
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int wave, int lane) const {
+    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
+      const int c = lane % TileGeom<D>::kChunks;
+      *reinterpret_cast<u32x4*>(tile + row * TileGeom<D>::kRowBytes + ((c ^ tile_swz<D>(row)) * 16)) = r[i];
+    }
+  }
+};
+
+}  // namespace fa

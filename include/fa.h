@@ -10,9 +10,10 @@
  * Hardware Scaling" (Key claims and Method): conditional rescaling of the
  * running output with threshold tau (paper §3.1.4, Eq. 6) and a software
  * 2^x (Cody-Waite range reduction + polynomial, paper §3.1.3, Table 2) for a
- * share of the exponentials.  The backward recomputes P from the LSE and uses
- * five matrix products per tile (paper §3.2.1, Eq. 7-8); its deterministic
- * mode fixes the order of the dQ accumulation (paper §1).
+ * share of the exponentials.  The backward recomputes P from the LSE and
+ * forms the gradients from the products of paper §3.2.1 (Eq. 7-8); every
+ * output is written once in a fixed order, so it is deterministic (the
+ * paper's deterministic mode, §1).
  *
  * Conventions shared by every entry point.
  *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA
@@ -75,24 +76,24 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  * the arguments are invalid. */
 float fa_fwd_realised_emu_frac(int d, float emu_frac);
 
-/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
- * [B,H,Sq,d], the row terms D_i = sum_c dO_ic O_ic [B,H,Sq] float32, and the
- * per-block turn counters of the deterministic mode.  0 on invalid sizes. */
+/* Bytes of device workspace fa_bwd needs: the row terms
+ * D_i = sum_c dO_ic O_ic, float32 [B,H,Sq] (rounded up to 256 bytes).
+ * 0 on invalid sizes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic);
 
 /* Backward.  Q, K, V, O, dO bf16 and LSE float32 in (O and LSE as written
  * by fa_fwd on the same inputs); dQ, dK, dV bf16 out.  P is recomputed from
  * LSE as exp(scale q.k - LSE); fp32 accumulation; outputs rounded to bf16
- * (nearest-even) once.
- *   deterministic  0: dQ contributions of different key blocks are added
- *                  with float atomics (order varies run to run).
- *                  1: they are added in ascending key-block order (a
- *                  per-query-block turn counter gates each addition), so
- *                  results are bit-identical run to run.
+ * (nearest-even) once.  dQ is produced by workgroups that own query rows and
+ * dK, dV by workgroups that own key rows, so every output element is written
+ * by exactly one workgroup in a fixed summation order (no atomics).
+ *   deterministic  0 or 1.  Results are bit-identical run to run in both
+ *                  modes; the paper's deterministic mode (ordered dQ
+ *                  accumulation, §1) is therefore met at no cost, and the
+ *                  flag selects the same kernels.
  *   workspace      device memory of at least fa_bwd_workspace_bytes(...);
- *                  its contents on entry do not matter (it is cleared on
- *                  `stream`); it must not be used concurrently by another
- *                  call.
+ *                  its contents on entry do not matter; it must not be used
+ *                  concurrently by another call.
  * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                  const void* dO, void* dQ, void* dK, void* dV,
