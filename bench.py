@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention hot path on one MI355X.
 
-One step = fa_fwd followed by fa_bwd (every step of the forward and the
-backward path) on the bwd workload: B=1, H=16, Sq=Sk=4096, d=128, causal,
-bf16 inputs drawn by workloads.py (seed 5), O and LSE taken from fa_fwd.
-Inputs and outputs are resident in device memory before timing starts.
+One step = fa_fwd followed by the backward (every step of the forward and
+the backward path) on the bwd workload: B=1, H=16, Sq=Sk=4096, d=128,
+causal, bf16 inputs drawn by workloads.py (seed 5), O and LSE taken from
+fa_fwd.  The backward is enqueued as its three kernels (fa_bwd_phase with
+PREPARE, DQ, DKDV: the same launches fa_bwd makes) with HIP events between
+them, on the stream the kernels run on, so each kernel's average duration is
+measured inside the timed region.  Inputs and outputs are resident in device
+memory before timing starts.
 
 Printed: ONE JSON line with the throughput in TFLOP/s (counted FLOPs:
 forward 4*B*H*S^2*d, backward 10*B*H*S^2*d, causal counts half), its share
@@ -45,7 +49,8 @@ def parse():
     p.add_argument("--fwd-only", action="store_true")
     p.add_argument("--reps", type=int, default=0, help="only run K steps (for profilers), print nothing else")
     p.add_argument("--copy-mib", type=int, default=0,
-                   help="only run --reps plain device copies of this many MiB (scales HBM counters)")
+                   help="with --reps: first run --reps plain device copies of this many MiB "
+                        "(a known byte count that scales the HBM counters)")
     return p.parse_args()
 
 
@@ -63,6 +68,39 @@ def time_calls(fn, n, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def kernel_sources_sha256():
+    """Hash of the HIP sources the kernels are built from (ties a counter
+    summary in profiles/ to the kernel version it measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_50_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<kernel>_<workload>.md
+    (FETCH_SIZE + WRITE_SIZE counters scaled by a plain copy of known size), or
+    None when no summary exists or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            key, val = line.strip()[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s):
@@ -128,59 +166,77 @@ def main():
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
                   deterministic=bool(args.deterministic))
 
-    if args.copy_mib:
-        src = torch.ones(args.copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(max(1, args.reps)):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"copied {args.copy_mib} MiB x {max(1, args.reps)}", flush=True)
-        return
     if args.reps:
+        # profiler mode: optional plain copies of known size (to scale HBM
+        # counters), then K steps; prints one line and nothing else
+        if args.copy_mib:
+            src = torch.ones(args.copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(args.reps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
         for _ in range(args.reps):
             fwd()
             if do_bwd:
                 bwd()
         torch.cuda.synchronize()
-        print(f"ran {args.reps} steps of {w.name}", flush=True)
+        print(f"ran {args.reps} steps of {w.name}" +
+              (f" after {args.reps} copies of {args.copy_mib} MiB" if args.copy_mib else ""), flush=True)
         return
 
-    # ---- warmup, then exactly K timed steps with per-kernel-call events
+    def bwd_phase(ph):
+        fa.fa_bwd_phase(ph, q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
+                        deterministic=bool(args.deterministic))
+
+    # the step, kernel by kernel (fa_bwd = the three phases in this order)
+    parts = [("fwd_kernel", fwd)]
+    if do_bwd:
+        parts += [("bwd_prep_kernel", lambda: bwd_phase(fa.FA_BWD_PREPARE)),
+                  ("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_DQ)),
+                  ("bwd_dkdv_kernel", lambda: bwd_phase(fa.FA_BWD_DKDV))]
+
+    # ---- warmup, then exactly K timed steps with events between kernels
     for _ in range(args.warmup):
-        fwd()
-        if do_bwd:
-            bwd()
+        for _, fn in parts:
+            fn()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     t_wall0 = time.perf_counter()
     for e in evs:
         e[0].record()
-        fwd()
-        e[1].record()
-        if do_bwd:
-            bwd()
-        e[2].record()
+        for i, (_, fn) in enumerate(parts):
+            fn()
+            e[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if do_bwd else 0.0
-    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
+    part_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(len(parts))]
+    step_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
 
+    # counted FLOPs (the configs' convention) and each kernel's own algorithmic
+    # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ); dK/dV
+    # kernel 8d (S, dP, dV, dK); prep: HBM bytes (read O and dO, write D)
+    pairs = w.flops("fwd") / (4 * d)
     f_fwd = w.flops("fwd")
     f_bwd = w.flops("bwd") if do_bwd else 0.0
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
-    kernels = {"fa_fwd": dict(ms=fwd_ms, flops=f_fwd)}
-    if do_bwd:
-        kernels["fa_bwd"] = dict(ms=bwd_ms, flops=f_bwd)
+    work = {"fwd_kernel": ("mfma", 4 * d * pairs), "bwd_dq_kernel": ("mfma", 6 * d * pairs),
+            "bwd_dkdv_kernel": ("mfma", 8 * d * pairs),
+            "bwd_prep_kernel": ("hbm", B * H * Sq * (2 * d * 2 + 4))}
+    kernels = {}
+    for (name, _), ms in zip(parts, part_ms):
+        bound, amount = work[name]
+        rate = amount / (ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+        kernels[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(rate, 2),
+                         "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(rate / peak, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    ach = kernels[dom]["flops"] / (kernels[dom]["ms"] * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "flops_per_launch": kernels[dom]["flops"], "avg_launch_ms": round(kernels[dom]["ms"], 5)}
-
-    detail = {n: {"ms": round(x["ms"], 5), "tflops": round(x["flops"] / (x["ms"] * 1e-3) / 1e12, 2),
-                  "pct_peak": round(100 * x["flops"] / (x["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
-              for n, x in kernels.items()}
+    kd = kernels[dom]
+    traffic = read_traffic(dom, w.name)
+    roof = {"bound": kd["bound"], "kernel": dom, "achieved": kd["achieved"],
+            "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS, "unit": kd["unit"],
+            "frac": kd["frac"], "traffic": traffic, "work_per_launch": work[dom][1],
+            "avg_launch_ms": kd["ms"]}
 
     extra = {}
     if not args.no_extra:
@@ -224,7 +280,7 @@ def main():
         "peak_tflops": PEAK_BF16_TFLOPS,
         "roofline": roof,
         "cpu_baseline": cpu,
-        "kernels": detail,
+        "kernels": kernels,
         "workloads_fwd": extra,
         "wall_s_timed": round(wall_s, 4),
     }

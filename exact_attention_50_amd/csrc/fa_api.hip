@@ -68,9 +68,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, i
   return fa::bwd_workspace_bytes(B, H, Sq, Sk, d, deterministic != 0);
 }
 
-fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
-                 void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d, int causal, float scale,
-                 int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+fa_status fa_bwd_phase(int phases, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                       const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d, int causal,
+                       float scale, int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+  if (phases < 1 || phases > FA_BWD_ALL) return FA_ERR_INVALID;
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID;
   const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV, workspace};
   for (const void* p : ptrs)
@@ -91,8 +92,15 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   a.scale = scale;
   a.deterministic = deterministic != 0;
   a.workspace = workspace;
-  const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = fa::launch_bwd(a, phases, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                 void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d, int causal, float scale,
+                 int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_phase(FA_BWD_ALL, Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Sq, Sk, d, causal, scale, deterministic,
+                      workspace, workspace_bytes, stream);
 }
 
 fa_status fa_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, void* stream) {

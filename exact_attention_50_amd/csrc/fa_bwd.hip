@@ -352,6 +352,7 @@ constexpr int kKW = 32;
 constexpr int kBK = kWaves * kKW;
 constexpr int kBQ = 64;
 constexpr int kStages = 2;
+constexpr int kAhead = 4;
 template <int D>
 struct Layout {
   static constexpr int kTileBytes = kBQ * TileGeom<D>::kRowBytes;
@@ -444,21 +445,61 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     const int q0 = qt * kBQ;
     // causal: skip tiles whose rows all precede the wave's keys
     if (!CAUSAL || k_wave_lo <= q0 + kBQ - 1) {
+      // Tile body as a short software pipeline over the two 32-row blocks b:
+      //   (1) S_0, dP_0            (2) S_1, dP_1  | P_0, dS_0 (VALU)
+      //   (3) dV, dK for rows 0-31 | P_1, dS_1    (4) dV, dK for rows 32-63
+      // so each block's VALU work overlaps the other block's MFMAs; LDS
+      // operands stream through a register ring.
       f32x16 s[2], dp[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      bf16x8 bp[kBQ / 16], bs[kBQ / 16];   // bf16 P and dS per 16-row step
+      const bool need_mask = (CAUSAL && k_wave_lo + kKW - 1 > q0) || (k0 + kBK > p.Sk);
+      // 2 kKC products: (S, dP) pairs over kc, alternating accumulators
+      auto sdp = [&](int b) __attribute__((always_inline)) {
         s[b] = f32x16{};
         dp[b] = f32x16{};
+        constexpr int kN = 2 * kKC;
+        auto op = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+          return (j & 1) ? read_rows<D>(otile, row_lane, b, j >> 1) : read_rows<D>(qtile, row_lane, b, j >> 1);
+        };
+        bf16x8 ring[kAhead];
 #pragma unroll
-        for (int kc = 0; kc < kKC; ++kc) {
-          s[b] = mfma32x32x16(read_rows<D>(qtile, row_lane, b, kc), kf[kc], s[b]);
-          dp[b] = mfma32x32x16(read_rows<D>(otile, row_lane, b, kc), vf[kc], dp[b]);
+        for (int j = 0; j < kAhead; ++j) ring[j] = op(j);
+#pragma unroll
+        for (int j = 0; j < kN; ++j) {
+          const bf16x8 a = ring[j % kAhead];
+          if (j + kAhead < kN) ring[j % kAhead] = op(j + kAhead);
+          if (j & 1) dp[b] = mfma32x32x16(a, vf[j >> 1], dp[b]);
+          else s[b] = mfma32x32x16(a, kf[j >> 1], s[b]);
         }
-      }
-      // P and dS (lane = key, 16 query rows per block)
-      const bool need_mask = (CAUSAL && k_wave_lo + kKW - 1 > q0) || (k0 + kBK > p.Sk);
+      };
+      // 2 kDB products per 16-row step, for steps ks0, ks0 + 1
+      auto dkdv = [&](int ks0) __attribute__((always_inline)) {
+        constexpr int kN = 2 * 2 * kDB;
+        auto op = [&](int j) __attribute__((always_inline)) -> bf16x8 {
+          const int ks = ks0 + (j / (2 * kDB)), db = (j >> 1) % kDB;
+          return (j & 1) ? read_cols<D>(qtile, tr_lane, ks, db) : read_cols<D>(otile, tr_lane, ks, db);
+        };
+        bf16x8 ring[kAhead];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int j = 0; j < kAhead; ++j) ring[j] = op(j);
+#pragma unroll
+        for (int j = 0; j < kN; ++j) {
+          const bf16x8 a = ring[j % kAhead];
+          if (j + kAhead < kN) ring[j % kAhead] = op(j + kAhead);
+          const int ks = ks0 + (j / (2 * kDB)), db = (j >> 1) % kDB;
+          if (j & 1) dk[db] = mfma32x32x16(a, bs[ks], dk[db]);
+          else dv[db] = mfma32x32x16(a, bp[ks], dv[db]);
+        }
+      };
+      auto mask = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + b * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if ((CAUSAL && key > q) || key >= p.Sk) s[b][i] = kNegInf;
+        }
+      };
+      // P = exp2(s scale log2e - LSE log2e), dS = P (dP - D), packed to bf16
+      auto pds = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = b * 32 + 8 * i4 + 4 * g;
@@ -467,26 +508,46 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 4 * i4 + j;
-            float pv = exp2_hw(__builtin_fmaf(s[b][i], p.scale_log2, -l4[j]));
-            if (need_mask && ((CAUSAL && key > q0 + r0 + j) || key >= p.Sk)) pv = 0.0f;
+            const float pv = exp2_hw(__builtin_fmaf(s[b][i], p.scale_log2, -l4[j]));
             s[b][i] = pv;
             dp[b][i] = pv * (dp[b][i] - d4[j]);
           }
         }
-      // dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
-      for (int ks = 0; ks < kBQ / 16; ++ks) {
-        const int b = ks >> 1, h = (ks & 1) * 8;
-        const bf16x8 bp = pack_bf16x8(s[b][h], s[b][h + 1], s[b][h + 2], s[b][h + 3], s[b][h + 4], s[b][h + 5],
-                                      s[b][h + 6], s[b][h + 7]);
-        const bf16x8 bs = pack_bf16x8(dp[b][h], dp[b][h + 1], dp[b][h + 2], dp[b][h + 3], dp[b][h + 4],
-                                      dp[b][h + 5], dp[b][h + 6], dp[b][h + 7]);
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          dv[db] = mfma32x32x16(read_cols<D>(otile, tr_lane, ks, db), bp, dv[db]);
-          dk[db] = mfma32x32x16(read_cols<D>(qtile, tr_lane, ks, db), bs, dk[db]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int h = hh * 8;
+          bp[2 * b + hh] = pack_bf16x8(s[b][h], s[b][h + 1], s[b][h + 2], s[b][h + 3], s[b][h + 4], s[b][h + 5],
+                                       s[b][h + 6], s[b][h + 7]);
+          bs[2 * b + hh] = pack_bf16x8(dp[b][h], dp[b][h + 1], dp[b][h + 2], dp[b][h + 3], dp[b][h + 4],
+                                       dp[b][h + 5], dp[b][h + 6], dp[b][h + 7]);
         }
+      };
+      sdp(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (need_mask) mask(0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1);
+      pds(0);
+#pragma unroll
+      for (int r = 0; r < 2 * kKC; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (need_mask) mask(1);
+      __builtin_amdgcn_sched_barrier(0);
+      dkdv(0);
+      pds(1);
+#pragma unroll
+      for (int r = 0; r < 4 * kDB; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dkdv(2);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (has_next) commit(stage ^ 1);
     lds_barrier();
@@ -520,22 +581,29 @@ hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int lds, hipStream_t stream
 }
 
 template <int D>
-hipError_t launch_all(const BwdArgs& a, BwdParams& prm, hipStream_t stream) {
+hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t stream) {
   prm.dvec = static_cast<float*>(a.workspace);
-  const long long rows = (long long)a.B * a.H * a.Sq;
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(1024), dim3(256), 0, stream, prm, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const dim3 gq((unsigned)(((a.Sq + dqk::kBM - 1) / dqk::kBM) * prm.BH));
-  e = a.causal ? launch_dyn(bwd_dq_kernel<D, true>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm)
-               : launch_dyn(bwd_dq_kernel<D, false>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm);
-  if (e != hipSuccess) return e;
-
-  const dim3 gk((unsigned)(((a.Sk + kvk::kBK - 1) / kvk::kBK) * prm.BH));
-  return a.causal
-             ? launch_dyn(bwd_dkdv_kernel<D, true>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm)
-             : launch_dyn(bwd_dkdv_kernel<D, false>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm);
+  hipError_t e = hipSuccess;
+  if (phases & kBwdPrepare) {
+    const long long rows = (long long)a.B * a.H * a.Sq;
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(1024), dim3(256), 0, stream, prm, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kBwdDq) {
+    const dim3 gq((unsigned)(((a.Sq + dqk::kBM - 1) / dqk::kBM) * prm.BH));
+    e = a.causal
+            ? launch_dyn(bwd_dq_kernel<D, true>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm)
+            : launch_dyn(bwd_dq_kernel<D, false>, gq, dim3(dqk::kThreads), dqk::Layout<D>::kLdsBytes, stream, prm);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kBwdDkdv) {
+    const dim3 gk((unsigned)(((a.Sk + kvk::kBK - 1) / kvk::kBK) * prm.BH));
+    e = a.causal
+            ? launch_dyn(bwd_dkdv_kernel<D, true>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm)
+            : launch_dyn(bwd_dkdv_kernel<D, false>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes, stream, prm);
+  }
+  return e;
 }
 
 }  // namespace
@@ -544,7 +612,7 @@ size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int /*d*/, bool /*d
   return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~size_t(255);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream) {
   BwdParams prm;
   prm.q = static_cast<const bf16*>(a.q);
   prm.k = static_cast<const bf16*>(a.k);
@@ -560,7 +628,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   prm.Sk = a.Sk;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale * kLog2e;
-  return a.d == 64 ? launch_all<64>(a, prm, stream) : launch_all<128>(a, prm, stream);
+  return a.d == 64 ? launch_all<64>(a, prm, phases, stream) : launch_all<128>(a, prm, phases, stream);
 }
 
 }  // namespace fa

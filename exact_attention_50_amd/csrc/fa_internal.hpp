@@ -44,7 +44,9 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, bool deterministic);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// phases: bit mask of the kernels to enqueue, in this order
+constexpr int kBwdPrepare = 1, kBwdDq = 2, kBwdDkdv = 4;
+hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);
 
 hipError_t launch_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, hipStream_t stream);
 

@@ -100,6 +100,23 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* The three kernels of fa_bwd, enqueued separately (a bit mask, executed in
+ * this order within one call):
+ *   FA_BWD_PREPARE  D_i = sum_c dO_ic O_ic into the workspace;
+ *   FA_BWD_DQ       dQ (reads D from the workspace; writes dQ only);
+ *   FA_BWD_DKDV     dK and dV (reads D; writes dK, dV only).
+ * After PREPARE has completed, DQ and DKDV are independent and may run on
+ * different streams (the caller orders them with events).  Arguments and
+ * validation are those of fa_bwd; fa_bwd is fa_bwd_phase(FA_BWD_ALL, ...). */
+#define FA_BWD_PREPARE 1
+#define FA_BWD_DQ 2
+#define FA_BWD_DKDV 4
+#define FA_BWD_ALL 7
+fa_status fa_bwd_phase(int phases, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                       const void* dO, void* dQ, void* dK, void* dV,
+                       int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Element-wise probe of the two exponentials the forward uses, so their
  * agreement can be measured (paper §3.1.3, Table 2): y_hw[i] = hardware
  * 2^x[i] (v_exp_f32), y_emu[i] = the software 2^x[i] of the forward kernel.

@@ -91,3 +91,14 @@ def test_exp2_probe_empty_is_noop(L):
     assert L.fa_exp2_probe(vp(0), vp(0), vp(0), 0, vp(0)) == fa.FA_OK
     assert L.fa_exp2_probe(vp(0), vp(0), vp(0), -1, vp(0)) == fa.FA_ERR_INVALID
     assert L.fa_exp2_probe(vp(0), vp(FAKE), vp(FAKE), 5, vp(0)) == fa.FA_ERR_INVALID
+
+
+def test_bwd_phase_mask_validation(L):
+    vp = ctypes.c_void_p
+    ws = fa.fa_bwd_workspace_bytes(1, 2, 100, 100, 64, True, True)
+    args = [vp(FAKE)] * 9 + [1, 2, 100, 100, 64, 1, 0.125, 1, vp(FAKE), ws, vp(0)]
+    for bad_mask in (0, 8, -1):
+        assert L.fa_bwd_phase(bad_mask, *args) == fa.FA_ERR_INVALID
+    bad = list(args)
+    bad[13] = 96   # d
+    assert L.fa_bwd_phase(fa.FA_BWD_DQ, *bad) == fa.FA_ERR_UNSUPPORTED

@@ -95,3 +95,32 @@ def test_workspace_reuse_and_dirty_workspace():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+def test_phases_separately_equal_fa_bwd(d, causal):
+    """fa_bwd_phase(PREPARE), then DQ, then DKDV (also DKDV before DQ) writes
+    the same bits as one fa_bwd call; DQ and DKDV each touch only their outputs."""
+    say(f"bwd phases d={d} causal={causal}")
+    q, k, v, do = (t.to(DEV) for t in make_inputs(1, 3, 333, 333, d, seed=40 + d, with_dout=True))
+    o, lse = fa.forward(q, k, v, causal=causal)
+    ref = fa.backward(q, k, v, o, lse, do, causal=causal)
+    nbytes = fa.fa_bwd_workspace_bytes(1, 3, 333, 333, d, causal, False)
+    for order in ((fa.FA_BWD_DQ, fa.FA_BWD_DKDV), (fa.FA_BWD_DKDV, fa.FA_BWD_DQ)):
+        ws = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+        outs = [torch.full_like(q, 7.0) for _ in range(3)]
+        fa.fa_bwd_phase(fa.FA_BWD_PREPARE, q, k, v, o, lse, do, *outs, ws, causal=causal)
+        torch.cuda.synchronize()
+        assert all(bool((t == 7.0).all()) for t in outs), "PREPARE wrote an output"
+        fa.fa_bwd_phase(order[0], q, k, v, o, lse, do, *outs, ws, causal=causal)
+        torch.cuda.synchronize()
+        first = (0,) if order[0] == fa.FA_BWD_DQ else (1, 2)
+        for i in range(3):
+            if i in first:
+                assert torch.equal(outs[i], ref[i])
+            else:
+                assert bool((outs[i] == 7.0).all())
+        fa.fa_bwd_phase(order[1], q, k, v, o, lse, do, *outs, ws, causal=causal)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
