@@ -215,14 +215,15 @@ def main():
 
     # counted FLOPs (the configs' convention) and each kernel's own algorithmic
     # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ); dK/dV
-    # kernel 8d (S, dP, dV, dK); prep: HBM bytes (read O and dO, write D)
+    # kernel 8d (S, dP, dV, dK); prep: HBM bytes (read O, dO and LSE, write D
+    # and LSE log2(e))
     pairs = w.flops("fwd") / (4 * d)
     f_fwd = w.flops("fwd")
     f_bwd = w.flops("bwd") if do_bwd else 0.0
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
     work = {"fwd_kernel": ("mfma", 4 * d * pairs), "bwd_dq_kernel": ("mfma", 6 * d * pairs),
             "bwd_dkdv_kernel": ("mfma", 8 * d * pairs),
-            "bwd_prep_kernel": ("hbm", B * H * Sq * (2 * d * 2 + 4))}
+            "bwd_prep_kernel": ("hbm", B * H * Sq * (2 * d * 2 + 3 * 4))}
     kernels = {}
     for (name, _), ms in zip(parts, part_ms):
         bound, amount = work[name]

@@ -20,7 +20,7 @@
 //                     S = Q K^T, dP = dO V^T (one key per lane), P, dS,
 //                     dV^T += dO^T P, dK^T += Q^T dS.
 // That is seven products per tile pair instead of five, no atomics, no
-// workspace beyond D, and results that are bit-identical run to run in both
+// workspace beyond the row terms D and LSE log2(e), and results that are bit-identical run to run in both
 // modes (the deterministic flag costs nothing).  Tiles use the layout of
 // fa_tiles.hpp, so Q, dO, K and V are each read both row-wise and transposed
 // from one LDS copy.
@@ -45,12 +45,14 @@ struct BwdParams {
   bf16* dk;
   bf16* dv;
   float* dvec;   // D_i, [B, H, Sq]
+  float* lse2;   // LSE_i * log2(e), [B, H, Sq]
   int BH, Sq, Sk;
   float scale;
   float scale_log2;
 };
 
 // ------------------------------------------------------------------- prep
+// D_i and LSE_i log2(e) of every query row into the workspace.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long rows) {
   // D_i = sum_c dO_ic O_ic: D/8 lanes per row, 16 bytes each
@@ -67,7 +69,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long ro
     for (int j = 0; j < 8; ++j) s = __builtin_fmaf((float)a[j], (float)b[j], s);
 #pragma unroll
     for (int off = kTPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if ((t % kTPR) == 0) p.dvec[row] = s;
+    if ((t % kTPR) == 0) {
+      p.dvec[row] = s;
+      p.lse2[row] = p.lse[row] * kLog2e;
+    }
   }
 }
 
@@ -343,31 +348,59 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // =================================================================== dK dV
-// 4 wavefronts x 32 keys = 128 keys per workgroup; query tiles of 64 rows in
-// a 2-stage LDS ring (register prefetch, one barrier per tile).
+// 4 wavefronts x 32 keys = 128 keys per workgroup (one wave per SIMD); query
+// tiles of 64 rows.  Per tile a wave runs one fixed sequence of kSteps MFMAs,
+//   [S, dP of rows 0-31] [S, dP of rows 32-63] [dV, dK of rows 0-31] [... 32-63]
+// whose LDS operands stream through a ring of kRing registers that runs on
+// across tiles, and whose P / dS arithmetic is spread element by element over
+// the MFMAs of the following block.  Tiles arrive memory-to-LDS in a 3-stage
+// ring, issued two tiles ahead; the one barrier per tile sits kRing steps
+// before the tile's end, once every operand of the tile has been read.
 namespace kvk {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKW = 32;
 constexpr int kBK = kWaves * kKW;
 constexpr int kBQ = 64;
-constexpr int kStages = 2;
-constexpr int kAhead = 4;
+constexpr int kStages = 3;
+constexpr int kRing = 8;
 template <int D>
 struct Layout {
   static constexpr int kTileBytes = kBQ * TileGeom<D>::kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kBQ * 4;   // Q, dO, LSE*log2e, D
+  // Q, dO, then four 64-float row blocks: LSE*log2e, D (waves 0, 1) and the
+  // same again (waves 2, 3 load a copy so every wave issues the same loads)
+  static constexpr int kRowsOff = 2 * kTileBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes + 4 * kBQ * 4;
   static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kLoadsPerTile = 2 * TileDMA<D, kBQ, kWaves>::kLoads + 1;   // per wave
 };
 }  // namespace kvk
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   using namespace kvk;
   using L = Layout<D>;
   using G = TileGeom<D>;
-  constexpr int kKC = D / 16;   // 16-dim steps of S and dP
-  constexpr int kDB = D / 32;   // 32-dim blocks of dK^T / dV^T
+  constexpr int kKC = D / 16;               // 16-dim steps of S and dP
+  constexpr int kDB = D / 32;               // 32-dim blocks of dK^T / dV^T
+  constexpr int kNS = 2 * kKC;              // MFMAs of S and dP per 32-row block
+  constexpr int kND = 2 * kDB;              // MFMAs of dV and dK per 16-row step
+  constexpr int kSteps = 2 * kNS + 4 * kND;
+  constexpr int kBar = kSteps - kRing;      // barrier position (before this step)
+  constexpr int kPPS = D == 128 ? 1 : 2;    // P/dS elements per step
+  constexpr int kPer = L::kLoadsPerTile;
+  // the row terms of both blocks are read before the barrier frees the stage,
+  // and every bf16 P / dS half is packed before its first dV / dK product
+  static_assert(2 * kNS + 2 + 12 / kPPS - 3 < kBar, "row terms read after the barrier");
+  static_assert(kNS + 2 + 7 / kPPS < 2 * kNS && kNS + 2 + 15 / kPPS < 2 * kNS + kND, "block 0 P/dS late");
+  static_assert(2 * kNS + 2 + 7 / kPPS < 2 * kNS + 2 * kND && 2 * kNS + 2 + 15 / kPPS < 2 * kNS + 3 * kND,
+                "block 1 P/dS late");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -379,8 +412,7 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   const int kb = blockIdx.x / p.BH;   // small key blocks (most work when causal) first
   const int bh = blockIdx.x % p.BH;
   const int k0 = kb * kBK;
-  const int k_wave_lo = k0 + wave * kKW;
-  const int key = k_wave_lo + r32;
+  const int key = k0 + wave * kKW + r32;
 
   const unsigned head_q = (unsigned)p.Sq * G::kRowBytes;
   const unsigned head_k = (unsigned)p.Sk * G::kRowBytes;
@@ -388,6 +420,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + (size_t)bh * p.Sq * D, head_q);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
+  // row terms: waves 0 and 2 load LSE*log2e, waves 1 and 3 load D
+  const __amdgpu_buffer_rsrc_t rrow =
+      make_rsrc(((wave & 1) ? p.dvec : p.lse2) + (size_t)bh * p.Sq, (unsigned)p.Sq * 4u);
 
   const int row_lane = row_lane_offset<D>(lane);
   const int tr_lane = tr_lane_offset<D>(lane);
@@ -399,6 +434,8 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     const unsigned off = (unsigned)key * G::kRowBytes + (kc * 16 + 8 * g) * 2;
     kf[kc] = __builtin_bit_cast(bf16x8, load16(rk, off));
     vf[kc] = __builtin_bit_cast(bf16x8, load16(rv, off));
+    // only ever MFMA operands: keep them in the AGPR file
+    asm volatile("" : "+a"(kf[kc]), "+a"(vf[kc]));
   }
 
   f32x16 dk[kDB], dv[kDB];
@@ -408,152 +445,142 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     dv[db] = f32x16{};
   }
 
+  // Tiles qt_lo .. n_qt-1.  qt_lo < n_qt always holds: causal requires
+  // Sq == Sk and k0 < Sk, so k0 / kBQ <= (Sq - 1) / kBQ.
   const int n_qt = (p.Sq + kBQ - 1) / kBQ;
   const int qt_lo = CAUSAL ? k0 / kBQ : 0;
+  const int n = n_qt - qt_lo;
 
-  TileIO<D, kBQ, kWaves> qio, oio;
-  float rowval = 0.0f;   // tid < kBQ: LSE*log2e of a row; kBQ <= tid < 2 kBQ: D of a row
-  auto fetch = [&](int qt) __attribute__((always_inline)) {
-    qio.fetch(rq, qt * kBQ, wave, lane);
-    oio.fetch(rdo, qt * kBQ, wave, lane);
-    const int r = qt * kBQ + (tid & (kBQ - 1));
-    const bool ok = r < p.Sq;
-    const size_t ri = (size_t)bh * p.Sq + (ok ? r : 0);
-    if (tid < kBQ) rowval = ok ? p.lse[ri] * kLog2e : __builtin_huge_valf();   // past the end: P = 0
-    else if (tid < 2 * kBQ) rowval = ok ? p.dvec[ri] : 0.0f;
+  auto stage_ptr = [&](int t) __attribute__((always_inline)) -> char* {
+    return smem + (t % kStages) * L::kStageBytes;
   };
-  auto commit = [&](int stage) __attribute__((always_inline)) {
-    char* st = smem + stage * L::kStageBytes;
-    qio.store(st, wave, lane);
-    oio.store(st + L::kTileBytes, wave, lane);
-    if (tid < 2 * kBQ) reinterpret_cast<float*>(st + 2 * L::kTileBytes)[tid] = rowval;
+  // memory-to-LDS loads of relative tile t: kPer per wave
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    char* st = stage_ptr(t);
+    const int q0 = (qt_lo + t) * kBQ;
+    TileDMA<D, kBQ, kWaves>::load(rq, q0, st, wave, lane);
+    TileDMA<D, kBQ, kWaves>::load(rdo, q0, st + L::kTileBytes, wave, lane);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rrow, (__attribute__((address_space(3))) void*)(st + L::kRowsOff + wave * kBQ * 4), 4,
+        (q0 + lane) * 4, 0, 0, 0);
   };
 
-  if (qt_lo < n_qt) {
-    fetch(qt_lo);
-    commit(0);
-  }
-  lds_barrier();
-
-  for (int qt = qt_lo; qt < n_qt; ++qt) {
-    const int stage = (qt - qt_lo) & 1;
-    const char* qtile = smem + stage * L::kStageBytes;
-    const char* otile = qtile + L::kTileBytes;
-    const float* rows = reinterpret_cast<const float*>(qtile + 2 * L::kTileBytes);
-    const bool has_next = qt + 1 < n_qt;
-    if (has_next) fetch(qt + 1);
-    const int q0 = qt * kBQ;
-    // causal: skip tiles whose rows all precede the wave's keys
-    if (!CAUSAL || k_wave_lo <= q0 + kBQ - 1) {
-      // Tile body as a short software pipeline over the two 32-row blocks b:
-      //   (1) S_0, dP_0            (2) S_1, dP_1  | P_0, dS_0 (VALU)
-      //   (3) dV, dK for rows 0-31 | P_1, dS_1    (4) dV, dK for rows 32-63
-      // so each block's VALU work overlaps the other block's MFMAs; LDS
-      // operands stream through a register ring.
-      f32x16 s[2], dp[2];
-      bf16x8 bp[kBQ / 16], bs[kBQ / 16];   // bf16 P and dS per 16-row step
-      const bool need_mask = (CAUSAL && k_wave_lo + kKW - 1 > q0) || (k0 + kBK > p.Sk);
-      // 2 kKC products: (S, dP) pairs over kc, alternating accumulators
-      auto sdp = [&](int b) __attribute__((always_inline)) {
-        s[b] = f32x16{};
-        dp[b] = f32x16{};
-        constexpr int kN = 2 * kKC;
-        auto op = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-          return (j & 1) ? read_rows<D>(otile, row_lane, b, j >> 1) : read_rows<D>(qtile, row_lane, b, j >> 1);
-        };
-        bf16x8 ring[kAhead];
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j) ring[j] = op(j);
-#pragma unroll
-        for (int j = 0; j < kN; ++j) {
-          const bf16x8 a = ring[j % kAhead];
-          if (j + kAhead < kN) ring[j % kAhead] = op(j + kAhead);
-          if (j & 1) dp[b] = mfma32x32x16(a, vf[j >> 1], dp[b]);
-          else s[b] = mfma32x32x16(a, kf[j >> 1], s[b]);
-        }
-      };
-      // 2 kDB products per 16-row step, for steps ks0, ks0 + 1
-      auto dkdv = [&](int ks0) __attribute__((always_inline)) {
-        constexpr int kN = 2 * 2 * kDB;
-        auto op = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-          const int ks = ks0 + (j / (2 * kDB)), db = (j >> 1) % kDB;
-          return (j & 1) ? read_cols<D>(qtile, tr_lane, ks, db) : read_cols<D>(otile, tr_lane, ks, db);
-        };
-        bf16x8 ring[kAhead];
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j) ring[j] = op(j);
-#pragma unroll
-        for (int j = 0; j < kN; ++j) {
-          const bf16x8 a = ring[j % kAhead];
-          if (j + kAhead < kN) ring[j % kAhead] = op(j + kAhead);
-          const int ks = ks0 + (j / (2 * kDB)), db = (j >> 1) % kDB;
-          if (j & 1) dk[db] = mfma32x32x16(a, bs[ks], dk[db]);
-          else dv[db] = mfma32x32x16(a, bp[ks], dv[db]);
-        }
-      };
-      auto mask = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + b * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if ((CAUSAL && key > q) || key >= p.Sk) s[b][i] = kNegInf;
-        }
-      };
-      // P = exp2(s scale log2e - LSE log2e), dS = P (dP - D), packed to bf16
-      auto pds = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = b * 32 + 8 * i4 + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rows + r0);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rows + kBQ + r0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * i4 + j;
-            const float pv = exp2_hw(__builtin_fmaf(s[b][i], p.scale_log2, -l4[j]));
-            s[b][i] = pv;
-            dp[b][i] = pv * (dp[b][i] - d4[j]);
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int h = hh * 8;
-          bp[2 * b + hh] = pack_bf16x8(s[b][h], s[b][h + 1], s[b][h + 2], s[b][h + 3], s[b][h + 4], s[b][h + 5],
-                                       s[b][h + 6], s[b][h + 7]);
-          bs[2 * b + hh] = pack_bf16x8(dp[b][h], dp[b][h + 1], dp[b][h + 2], dp[b][h + 3], dp[b][h + 4],
-                                       dp[b][h + 5], dp[b][h + 6], dp[b][h + 7]);
-        }
-      };
-      sdp(0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (need_mask) mask(0);
-      __builtin_amdgcn_sched_barrier(0);
-      sdp(1);
-      pds(0);
-#pragma unroll
-      for (int r = 0; r < 2 * kKC; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (need_mask) mask(1);
-      __builtin_amdgcn_sched_barrier(0);
-      dkdv(0);
-      pds(1);
-#pragma unroll
-      for (int r = 0; r < 4 * kDB; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dkdv(2);
-      __builtin_amdgcn_sched_barrier(0);
+  // operand j of a tile (j < 2 kNS: row reads of Q / dO for S / dP; then
+  // transposed reads of dO / Q for dV / dK)
+  auto op = [&](const char* st, int j) __attribute__((always_inline)) -> bf16x8 {
+    const char* qtile = st;
+    const char* otile = st + L::kTileBytes;
+    if (j < 2 * kNS) {
+      const int b = j / kNS, jj = j % kNS;
+      return (jj & 1) ? read_rows<D>(otile, row_lane, b, jj >> 1) : read_rows<D>(qtile, row_lane, b, jj >> 1);
     }
-    if (has_next) commit(stage ^ 1);
-    lds_barrier();
+    const int jj = j - 2 * kNS;
+    const int ks = jj / kND, db = (jj >> 1) % kDB;
+    return (jj & 1) ? read_cols<D>(qtile, tr_lane, ks, db) : read_cols<D>(otile, tr_lane, ks, db);
+  };
+
+  // ---- prologue: tiles 0, 1, 2 in flight; wait for tile 0
+  issue(0);
+  if (n > 1) issue(1);
+  if (n > 2) issue(2);
+  if (n > 2) wait_vmcnt<2 * kPer>();
+  else if (n > 1) wait_vmcnt<kPer>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  bf16x8 ring[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) ring[j] = op(stage_ptr(0), j);
+
+  for (int t = 0; t < n; ++t) {
+    const char* cur = stage_ptr(t);
+    const char* nxt = stage_ptr(t + 1);
+    const int q0 = (qt_lo + t) * kBQ;
+    const float* lrow = reinterpret_cast<const float*>(cur + L::kRowsOff);   // LSE*log2e
+    const float* drow = lrow + kBQ;                                           // D
+    f32x16 s[2], dp[2];
+    bf16x8 bp[4], bs[4];      // bf16 P and dS of the four 16-row steps
+    float pe[16], de[16];     // P and dS of the block in progress
+    f32x4 l4[4], d4[4];       // LSE*log2e and D of its 16 rows
+    // causal: element i of block b is masked iff key - q0 - 32 b - 4 g > 8 (i / 4) + i % 4
+    const int delta0 = key - q0 - 4 * g;
+
+    static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      if constexpr (j == kBar) {
+        // every operand of tile t has been read; publish tile t + 1 (its
+        // loads were issued two tiles ago; those of t + 2 may still run)
+        if (t + 2 < n) wait_vmcnt<kPer>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 3 < n) issue(t + 3);
+      }
+      const bf16x8 a = ring[j % kRing];
+      if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, j + kRing);
+      else ring[j % kRing] = op(nxt, j + kRing - kSteps);
+      // S, dP accumulate in VGPRs (read by the P / dS arithmetic), dK, dV in
+      // AGPRs (read once, at the end); K and V are AGPR operands
+      if constexpr (j < 2 * kNS) {
+        constexpr int b = j / kNS, jj = j % kNS;
+        if constexpr (jj < 2) {
+          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::init_v(dp[b], a, vf[jj >> 1]);
+          else MfmaAsm<'v', 'a'>::init_v(s[b], a, kf[jj >> 1]);
+        } else {
+          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::acc_v(dp[b], a, vf[jj >> 1]);
+          else MfmaAsm<'v', 'a'>::acc_v(s[b], a, kf[jj >> 1]);
+        }
+      } else {
+        constexpr int jj = j - 2 * kNS;
+        constexpr int ks = jj / kND, db = (jj >> 1) % kDB;
+        if constexpr (jj & 1) MfmaAsm<'v', 'v'>::acc_a(dk[db], a, bs[ks]);
+        else MfmaAsm<'v', 'v'>::acc_a(dv[db], a, bp[ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // P / dS of block b, elements from step (b + 1) kNS + 2 on
+      static_for<2>([&](auto B) __attribute__((always_inline)) {
+        constexpr int b = B;
+        constexpr int first = (b + 1) * kNS + 2;
+        // row terms of elements 4 i4 .. 4 i4 + 3, three steps before their use
+        static_for<4>([&](auto I4) __attribute__((always_inline)) {
+          constexpr int i4 = I4;
+          if constexpr (j == first + (4 * i4) / kPPS - 3) {
+            l4[i4] = *reinterpret_cast<const f32x4*>(lrow + 32 * b + 8 * i4 + 4 * g);
+            d4[i4] = *reinterpret_cast<const f32x4*>(drow + 32 * b + 8 * i4 + 4 * g);
+          }
+        });
+        // the last S / dP products of block b were issued two and three steps ago
+        if constexpr (j == first) mfma_drain_v2(s[b], dp[b]);
+        static_for<kPPS>([&](auto U) __attribute__((always_inline)) {
+          constexpr int i = (j - first) * kPPS + U;
+          if constexpr (i >= 0 && i < 16) {
+            float x = __builtin_fmaf(s[b][i], p.scale_log2, -l4[i >> 2][i & 3]);
+            if (CAUSAL && delta0 - 32 * b > 8 * (i >> 2) + (i & 3)) x = kNegInf;
+            const float pv = exp2_hw(x);
+            pe[i] = pv;
+            de[i] = pv * (dp[b][i] - d4[i >> 2][i & 3]);
+            if constexpr ((i & 7) == 7) {
+              constexpr int h = i - 7;
+              bp[2 * b + (i >> 3)] = pack_bf16x8(pe[h], pe[h + 1], pe[h + 2], pe[h + 3], pe[h + 4], pe[h + 5],
+                                                 pe[h + 6], pe[h + 7]);
+              bs[2 * b + (i >> 3)] = pack_bf16x8(de[h], de[h + 1], de[h + 2], de[h + 3], de[h + 4], de[h + 5],
+                                                 de[h + 6], de[h + 7]);
+              // keep this work at this step (the IR optimiser would sink it
+              // next to the products that use it)
+              asm volatile("" ::"v"(bp[2 * b + (i >> 3)]), "v"(bs[2 * b + (i >> 3)]));
+            }
+          }
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
   // ---- dK = scale (dK^T)^T, dV = (dV^T)^T -> bf16 (lane = key)
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    mfma_drain_a(dk[db]);
+    mfma_drain_a(dv[db]);
+  }
   if (key < p.Sk) {
     bf16* dkr = p.dk + ((size_t)bh * p.Sk + key) * D;
     bf16* dvr = p.dv + ((size_t)bh * p.Sk + key) * D;
@@ -582,7 +609,10 @@ hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int lds, hipStream_t stream
 
 template <int D>
 hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t stream) {
+  // workspace: D [B H Sq] then LSE log2(e) [B H Sq], each rounded to 256 bytes
+  const size_t sec = ((size_t)a.B * a.H * a.Sq * sizeof(float) + 255) & ~size_t(255);
   prm.dvec = static_cast<float*>(a.workspace);
+  prm.lse2 = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + sec);
   hipError_t e = hipSuccess;
   if (phases & kBwdPrepare) {
     const long long rows = (long long)a.B * a.H * a.Sq;
@@ -609,7 +639,7 @@ hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t 
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int /*d*/, bool /*deterministic*/) {
-  return (((size_t)B * H * Sq * sizeof(float)) + 255) & ~size_t(255);
+  return 2 * ((((size_t)B * H * Sq * sizeof(float)) + 255) & ~size_t(255));
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream) {

@@ -9,6 +9,9 @@
 // so an accumulator column belongs to one lane pair (l, l^32).
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +34,47 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product written out as one instruction with the register file of
+// every operand fixed ("v": VGPR, "a": AGPR), for loops where the register
+// allocator would otherwise move accumulators between the two files.  The
+// compiler does not know these are MFMAs, so the callers handle the latencies
+// it would otherwise cover:
+//   * the leading s_nop gives the wait states a VALU write of an input needs
+//     before an MFMA reads it;
+//   * mfma_drain() (>= 20 wait states, tied to the accumulator so that no read
+//     is scheduled above it) must separate the last product into an
+//     accumulator from any VALU read of it.
+// A product into the same accumulator as the previous one needs nothing
+// (srcC is exactly the previous vdst).
+template <char CA, char CB>
+struct MfmaAsm;
+#define FA_MFMA_ASM(CA, CB, SA, SB)                                                                      \
+  template <>                                                                                            \
+  struct MfmaAsm<CA, CB> {                                                                               \
+    __device__ __forceinline__ static void init_v(f32x16& d, bf16x8 a, bf16x8 b) {                       \
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : SA(a), SB(b));        \
+    }                                                                                                    \
+    __device__ __forceinline__ static void acc_v(f32x16& d, bf16x8 a, bf16x8 b) {                        \
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : SA(a), SB(b));       \
+    }                                                                                                    \
+    __device__ __forceinline__ static void acc_a(f32x16& d, bf16x8 a, bf16x8 b) {                        \
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : SA(a), SB(b));       \
+    }                                                                                                    \
+  };
+FA_MFMA_ASM('v', 'v', "v", "v")
+FA_MFMA_ASM('v', 'a', "v", "a")
+#undef FA_MFMA_ASM
+
+__device__ __forceinline__ void mfma_drain_v(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+}
+__device__ __forceinline__ void mfma_drain_v2(f32x16& a0, f32x16& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(a0), "+v"(a1));
+}
+__device__ __forceinline__ void mfma_drain_a(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(acc));
 }
 
 // Hardware 2^x (v_exp_f32).  -inf and inputs below the normal range give 0.
@@ -87,9 +131,27 @@ __device__ __forceinline__ bf16x4_t lds_read_tr16(const void* lds_addr) {
       (__attribute__((address_space(3))) bf16x4_t*)(lds_addr));
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in order,
+// every index a compile-time constant (unrolling that does not depend on the
+// optimiser's size limits).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Workgroup barrier that waits for this wave's LDS operations only (global
 // prefetches stay in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup barrier that also waits for this wave's memory-to-LDS loads (and
+// every other vector-memory load of the wave).
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Round eight floats to bf16 (nearest-even) and pack them as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,

@@ -100,4 +100,31 @@ struct TileIO {
   }
 };
 
+// The same tile share loaded straight from memory into LDS (gfx950's
+// 16-byte buffer_load ... lds).  One such load writes 64 x 16 contiguous LDS
+// bytes, lane i at the uniform base + 16 i, i.e. RowsPerLoad whole rows; so
+// lane i fetches the global chunk that belongs at its LDS position: chunk
+// (i % Chunks) ^ f(row) of the row.  Rows at or past the descriptor's end
+// are written as zeros.  The writes complete with the wave's vector-memory
+// counter: wait for vmcnt(0), then a barrier, before other waves read them.
+template <int D, int ROWS, int NW>
+struct TileDMA {
+  static constexpr int kLoads = ROWS / TileGeom<D>::kRowsPerLoad / NW;
+  static_assert(kLoads >= 1, "tile too small for the workgroup");
+
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
+    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
+    constexpr int C = TileGeom<D>::kChunks;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int blk = i * NW + wave;   // wave-uniform
+      const int row = blk * RPL + lane / C;
+      const unsigned off = (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + ((lane % C) ^ tile_swz<D>(row)) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src, (__attribute__((address_space(3))) void*)(tile + blk * RPL * TileGeom<D>::kRowBytes), 16,
+          (int)off, 0, 0, 0);
+    }
+  }
+};
+
 }  // namespace fa
