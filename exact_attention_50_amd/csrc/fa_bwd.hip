@@ -393,6 +393,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   constexpr int kND = 2 * kDB;              // MFMAs of dV and dK per 16-row step
   constexpr int kSteps = 2 * kNS + 4 * kND;
   constexpr int kBar = kSteps - kRing;      // barrier position (before this step)
+  // operand j of any tile sits in ring slot j % kRing only if every tile
+  // starts on slot 0
+  static_assert(kSteps % kRing == 0, "ring must divide the step count");
   constexpr int kPPS = D == 128 ? 1 : 2;    // P/dS elements per step
   constexpr int kPer = L::kLoadsPerTile;
   // the row terms of both blocks are read before the barrier frees the stage,
@@ -434,8 +437,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     const unsigned off = (unsigned)key * G::kRowBytes + (kc * 16 + 8 * g) * 2;
     kf[kc] = __builtin_bit_cast(bf16x8, load16(rk, off));
     vf[kc] = __builtin_bit_cast(bf16x8, load16(rv, off));
-    // only ever MFMA operands: keep them in the AGPR file
-    asm volatile("" : "+a"(kf[kc]), "+a"(vf[kc]));
+    // only ever MFMA operands: keep them in the AGPR file (the s_nop covers
+    // the wait states between the moves and a first product right after)
+    asm volatile("s_nop 1" : "+a"(kf[kc]), "+a"(vf[kc]));
   }
 
   f32x16 dk[kDB], dv[kDB];
@@ -443,6 +447,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   for (int db = 0; db < kDB; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
+    // the zeros are VALU writes: fix them here, two wait states ahead of the
+    // first product (otherwise they sink next to it)
+    asm volatile("s_nop 1" : "+a"(dk[db]), "+a"(dv[db]));
   }
 
   // Tiles qt_lo .. n_qt-1.  qt_lo < n_qt always holds: causal requires
@@ -451,12 +458,12 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   const int qt_lo = CAUSAL ? k0 / kBQ : 0;
   const int n = n_qt - qt_lo;
 
-  auto stage_ptr = [&](int t) __attribute__((always_inline)) -> char* {
-    return smem + (t % kStages) * L::kStageBytes;
-  };
-  // memory-to-LDS loads of relative tile t: kPer per wave
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    char* st = stage_ptr(t);
+  // relative tile t lives in stage t % kStages; the stage is always a
+  // compile-time constant below, so every LDS address is a loop-invariant
+  // lane offset plus an immediate
+  // memory-to-LDS loads of relative tile t into stage S: kPer per wave
+  auto issue = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    char* st = smem + decltype(stage_tag)::value * L::kStageBytes;
     const int q0 = (qt_lo + t) * kBQ;
     TileDMA<D, kBQ, kWaves>::load(rq, q0, st, wave, lane);
     TileDMA<D, kBQ, kWaves>::load(rdo, q0, st + L::kTileBytes, wave, lane);
@@ -479,21 +486,30 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     return (jj & 1) ? read_cols<D>(qtile, tr_lane, ks, db) : read_cols<D>(otile, tr_lane, ks, db);
   };
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(kStages == 3, "stage constants below assume three stages");
+
   // ---- prologue: tiles 0, 1, 2 in flight; wait for tile 0
-  issue(0);
-  if (n > 1) issue(1);
-  if (n > 2) issue(2);
+  issue(0, S0{});
+  if (n > 1) issue(1, S1{});
+  if (n > 2) issue(2, S2{});
   if (n > 2) wait_vmcnt<2 * kPer>();
   else if (n > 1) wait_vmcnt<kPer>();
   else wait_vmcnt<0>();
   lds_barrier();
   bf16x8 ring[kRing];
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) ring[j] = op(stage_ptr(0), j);
+  for (int j = 0; j < kRing; ++j) ring[j] = op(smem, j);
 
-  for (int t = 0; t < n; ++t) {
-    const char* cur = stage_ptr(t);
-    const char* nxt = stage_ptr(t + 1);
+  // One tile; MASK: apply the causal mask (only the first kBK / kBQ tiles of
+  // a causal key block hold keys after some of their rows).
+  auto tile = [&](int t, auto mask_tag, auto stage_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int kS = decltype(stage_tag)::value;   // == t % kStages
+    const char* cur = smem + kS * L::kStageBytes;
+    const char* nxt = smem + ((kS + 1) % kStages) * L::kStageBytes;
     const int q0 = (qt_lo + t) * kBQ;
     const float* lrow = reinterpret_cast<const float*>(cur + L::kRowsOff);   // LSE*log2e
     const float* drow = lrow + kBQ;                                           // D
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
         else wait_vmcnt<0>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 3 < n) issue(t + 3);
+        if (t + 3 < n) issue(t + 3, stage_tag);
       }
       const bf16x8 a = ring[j % kRing];
       if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, j + kRing);
@@ -554,7 +570,7 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
           constexpr int i = (j - first) * kPPS + U;
           if constexpr (i >= 0 && i < 16) {
             float x = __builtin_fmaf(s[b][i], p.scale_log2, -l4[i >> 2][i & 3]);
-            if (CAUSAL && delta0 - 32 * b > 8 * (i >> 2) + (i & 3)) x = kNegInf;
+            if (MASK && delta0 - 32 * b > 8 * (i >> 2) + (i & 3)) x = kNegInf;
             const float pv = exp2_hw(x);
             pe[i] = pv;
             de[i] = pv * (dp[b][i] - d4[i >> 2][i & 3]);
@@ -573,6 +589,22 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
       });
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+  // tiles 0 and 1 (stages 0, 1; masked if causal), then the rest from stage
+  // 2 on, three tiles per loop pass
+  static_assert(kBK / kBQ == 2, "two masked tiles per causal key block");
+  using M = std::integral_constant<bool, CAUSAL>;
+  using F = std::false_type;
+  tile(0, M{}, S0{});
+  if (n > 1) tile(1, M{}, S1{});
+  int t = 2;
+  while (t < n) {
+    tile(t, F{}, S2{});
+    if (++t >= n) break;
+    tile(t, F{}, S0{});
+    if (++t >= n) break;
+    tile(t, F{}, S1{});
+    ++t;
   }
 
   // ---- dK = scale (dK^T)^T, dV = (dV^T)^T -> bf16 (lane = key)

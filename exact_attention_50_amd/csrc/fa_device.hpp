@@ -39,12 +39,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 // The same product written out as one instruction with the register file of
 // every operand fixed ("v": VGPR, "a": AGPR), for loops where the register
 // allocator would otherwise move accumulators between the two files.  The
-// compiler does not know these are MFMAs, so the callers handle the latencies
-// it would otherwise cover:
-//   * the leading s_nop gives the wait states a VALU write of an input needs
-//     before an MFMA reads it;
-//   * mfma_drain() (>= 20 wait states, tied to the accumulator so that no read
-//     is scheduled above it) must separate the last product into an
+// compiler does not know these are MFMAs, so two latencies it would cover
+// are the caller's:
+//   * a VALU write of an input needs two wait states before the MFMA reads
+//     it: callers produce inputs well ahead (ring loads, packed P / dS), and
+//     tests/test_kernel_asm.py checks the built code for such pairs;
+//   * mfma_drain_*() (>= 20 wait states, tied to the accumulator so that no
+//     read is scheduled above it) must separate the last product into an
 //     accumulator from any VALU read of it.
 // A product into the same accumulator as the previous one needs nothing
 // (srcC is exactly the previous vdst).
@@ -54,13 +55,13 @@ struct MfmaAsm;
   template <>                                                                                            \
   struct MfmaAsm<CA, CB> {                                                                               \
     __device__ __forceinline__ static void init_v(f32x16& d, bf16x8 a, bf16x8 b) {                       \
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : SA(a), SB(b));        \
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : SA(a), SB(b));        \
     }                                                                                                    \
     __device__ __forceinline__ static void acc_v(f32x16& d, bf16x8 a, bf16x8 b) {                        \
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : SA(a), SB(b));       \
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : SA(a), SB(b));       \
     }                                                                                                    \
     __device__ __forceinline__ static void acc_a(f32x16& d, bf16x8 a, bf16x8 b) {                        \
-      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : SA(a), SB(b));       \
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : SA(a), SB(b));       \
     }                                                                                                    \
   };
 FA_MFMA_ASM('v', 'v', "v", "v")
