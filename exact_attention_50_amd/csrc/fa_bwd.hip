@@ -76,24 +76,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, long long ro
   }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ==================================================================== dQ
-// 8 wavefronts x 32 query rows; the two groups of four (one wave of each per
-// SIMD) alternate between a matrix phase and a vector phase as in the
-// forward kernel, one barrier per phase, raised priority in matrix phases.
+// 4 wavefronts x 32 query rows = 128 rows per workgroup (one wave per SIMD);
+// key tiles of 64 rows, walked from the diagonal down (the two tiles that
+// can need a mask come first).  Work is pipelined by 32-key half tiles u:
+//   [S^T, dP^T of u  |  P, dS of u-1 (VALU)]  [dQ^T += K^T dS^T of u-1]
+// so a tile is [S,dP b0 | P,dS of the previous tile's b1] [dQ prev b1]
+// [S,dP b1 | P,dS b0] [dQ b0], one fixed sequence of MFMAs whose LDS operands
+// stream through a register ring running on across tiles.  K / V tiles
+// arrive memory-to-LDS in a 4-stage ring issued three tiles ahead (a tile's
+// K is still read during the next tile), one barrier per tile.
 namespace dqk {
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;
 constexpr int kBM = kWaves * kQW;
+constexpr int kBN = 64;
 constexpr int kStages = 4;
-constexpr int kAhead = 4;
+constexpr int kRing = 8;
 template <int D>
 struct Layout {
-  // keys per tile: 32 at d = 128 keeps a wave within 256 registers
-  static constexpr int kBN = D == 128 ? 32 : 64;
   static constexpr int kTileBytes = kBN * TileGeom<D>::kRowBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;   // K then V
   static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kLoadsPerTile = 2 * TileDMA<D, kBN, kWaves>::kLoads;   // per wave
 };
 }  // namespace dqk
 
@@ -102,26 +114,31 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   using namespace dqk;
   using L = Layout<D>;
   using G = TileGeom<D>;
-  constexpr int kBN = L::kBN;
-  constexpr int kKB = kBN / 32;   // 32-key blocks per tile
-  constexpr int kKS = kBN / 16;   // 16-key steps of K^T dS^T
-  constexpr int kDB = D / 32;     // 32-dim blocks of dQ^T
-  constexpr int kKC = D / 16;     // 16-dim steps of S^T and dP^T
-  constexpr int kNQ = kKS * kDB;  // dQ products per tile
-  constexpr int kNS = kKB * kKC;  // S^T (and as many dP^T) products per tile
+  constexpr int kKC = D / 16;           // 16-dim steps of S^T and dP^T
+  constexpr int kDB = D / 32;           // 32-dim blocks of dQ^T
+  constexpr int kNS = 2 * kKC;          // S^T and dP^T products of a half tile
+  constexpr int kNQ = 2 * kDB;          // dQ^T products of a half tile
+  constexpr int kU = kNS + kNQ;         // steps of a half tile
+  constexpr int kSteps = 2 * kU;
+  constexpr int kBar = kSteps - kRing;  // barrier position (before this step)
+  constexpr int kPPS = 16 / kNS;        // P / dS elements per step
+  constexpr int kPer = L::kLoadsPerTile;
+  static_assert(kSteps % kRing == 0, "ring must divide the step count");
+  static_assert(kRing <= kNS, "the ring's look-ahead into the next tile stays in its first S / dP block");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int group = wave >> 2;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  const int n_qblocks = (p.Sq + kBM - 1) / kBM;
-  const int rank = blockIdx.x / p.BH;
+  const int n_qb = (p.Sq + kBM - 1) / kBM;
+  const int qb = CAUSAL ? n_qb - 1 - (int)(blockIdx.x / p.BH) : (int)(blockIdx.x / p.BH);   // heavy first
   const int bh = blockIdx.x % p.BH;
-  const int qb = CAUSAL ? (n_qblocks - 1 - rank) : rank;
+  const int q0 = qb * kBM;
+  const int qi = q0 + wave * kQW + r32;   // the lane's query row
+  const bool q_ok = qi < p.Sq;
 
   const unsigned head_q = (unsigned)p.Sq * G::kRowBytes;
   const unsigned head_k = (unsigned)p.Sk * G::kRowBytes;
@@ -130,212 +147,202 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
 
-  const int q_wave_lo = qb * kBM + wave * kQW;
-  const int q_lane = q_wave_lo + r32;
   const int row_lane = row_lane_offset<D>(lane);
   const int tr_lane = tr_lane_offset<D>(lane);
 
-  // B operands: Q^T and dO^T of the lane's query, dims 16 kc + 8 g .. +8
+  // B operands: the lane's Q and dO rows, dims 16 kc + 8 g .. +8 (AGPRs)
   bf16x8 qf[kKC], of[kKC];
 #pragma unroll
   for (int kc = 0; kc < kKC; ++kc) {
-    const unsigned off = (unsigned)q_lane * G::kRowBytes + (kc * 16 + 8 * g) * 2;
+    const unsigned off = (unsigned)qi * G::kRowBytes + (kc * 16 + 8 * g) * 2;
     qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, off));
     of[kc] = __builtin_bit_cast(bf16x8, load16(rdo, off));
+    asm volatile("s_nop 1" : "+a"(qf[kc]), "+a"(of[kc]));
   }
-  const bool q_ok = q_lane < p.Sq;
-  const size_t qi = (size_t)bh * p.Sq + (q_ok ? q_lane : 0);
-  const float lse2 = q_ok ? p.lse[qi] * kLog2e : __builtin_huge_valf();   // rows past the end: P = 0
-  const float dval = q_ok ? p.dvec[qi] : 0.0f;
-
-  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM) : p.Sk;
-  const int n = (kv_end + kBN - 1) / kBN;
-  const int n_wave = CAUSAL ? min(n, (q_wave_lo + kQW - 1) / kBN + 1) : n;
+  // the lane's row terms (rows past the end: any finite value; never stored)
+  const size_t ri = (size_t)bh * p.Sq + (q_ok ? qi : 0);
+  const float lse2 = p.lse2[ri];
+  const float dval = p.dvec[ri];
 
   f32x16 dq[kDB];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) dq[db] = f32x16{};
-  f32x16 s[kKB], dp[kKB];
-  bf16x8 pk[kKS];   // dS^T in bf16: B operands of K^T dS^T
+  for (int db = 0; db < kDB; ++db) {
+    dq[db] = f32x16{};
+    asm volatile("s_nop 1" : "+a"(dq[db]));
+  }
 
-  // ---- matrix phase: dQ^T += K_{t-1}^T dS_{t-1}^T, then S_t^T = K_t Q^T and
-  // dP_t^T = V_t dO^T; one stream of MFMAs whose LDS operands are read
-  // kAhead ahead through a register ring.
-  auto matrix_body = [&](int t, auto with_dq, auto with_s) __attribute__((always_inline)) {
-    constexpr bool DQ = decltype(with_dq)::value;
-    constexpr bool SP = decltype(with_s)::value;
-    constexpr int j0 = DQ ? 0 : kNQ;
-    constexpr int j1 = SP ? kNQ + 2 * kNS : kNQ;
-    const char* kprev = smem + ((t + kStages - 1) % kStages) * L::kStageBytes;
-    const char* kcur = smem + (t % kStages) * L::kStageBytes;
-    const char* vcur = kcur + L::kTileBytes;
-    // j < kNQ: (ks, db) = (j / kDB, j % kDB); then pairs (S, dP) for (kc, kb)
-    auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
-      if (j < kNQ) return read_cols<D>(kprev, tr_lane, j / kDB, j % kDB);
-      const int i = (j - kNQ) >> 1;
-      const int kb = i % kKB, kc = i / kKB;
-      return ((j - kNQ) & 1) ? read_rows<D>(vcur, row_lane, kb, kc) : read_rows<D>(kcur, row_lane, kb, kc);
-    };
-    if (SP) {
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-      }
+  // key tiles: n of them, relative tile t is key tile n - 1 - t
+  const int n_kt_all = (p.Sk + kBN - 1) / kBN;
+  const int n_kt_causal = (q0 + kBM + kBN - 1) / kBN;
+  const int n = CAUSAL ? (n_kt_causal < n_kt_all ? n_kt_causal : n_kt_all) : n_kt_all;
+
+  auto issue = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    char* st = smem + decltype(stage_tag)::value * L::kStageBytes;
+    const int k0 = (n - 1 - t) * kBN;
+    TileDMA<D, kBN, kWaves>::load(rk, k0, st, wave, lane);
+    TileDMA<D, kBN, kWaves>::load(rv, k0, st + L::kTileBytes, wave, lane);
+  };
+
+  // operand j of a tile: [rows of K, V block 0][cols of the previous tile's
+  // K, steps 2, 3][rows of K, V block 1][cols of this tile's K, steps 0, 1]
+  auto op = [&](const char* cur, const char* prev, int j) __attribute__((always_inline)) -> bf16x8 {
+    const int u = j / kU, jj = j % kU;
+    if (jj < kNS) {
+      const char* tile = (jj & 1) ? cur + L::kTileBytes : cur;
+      return read_rows<D>(tile, row_lane, u, jj >> 1);
     }
-    bf16x8 ring[kAhead];
+    const int qj = jj - kNS;
+    const int ks = 2 * (1 - u) + qj / kDB, db = qj % kDB;
+    return read_cols<D>(u == 0 ? prev : cur, tr_lane, ks, db);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  static_assert(kStages == 4, "stage constants below assume four stages");
+
+  // ---- prologue: tiles 0, 1, 2 in flight; wait for tile 0
+  issue(0, S0{});
+  if (n > 1) issue(1, S1{});
+  if (n > 2) issue(2, S2{});
+  if (n > 2) wait_vmcnt<2 * kPer>();
+  else if (n > 1) wait_vmcnt<kPer>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  bf16x8 ring[kRing];
 #pragma unroll
-    for (int j = j0; j < j0 + kAhead && j < j1; ++j) ring[(j - j0) % kAhead] = operand(j);
-#pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      const bf16x8 a = ring[(j - j0) % kAhead];
-      if (j + kAhead < j1) ring[(j - j0) % kAhead] = operand(j + kAhead);
-      if (j < kNQ) {
-        dq[j % kDB] = mfma32x32x16(a, pk[j / kDB], dq[j % kDB]);
-      } else {
-        const int i = (j - kNQ) >> 1;
-        const int kb = i % kKB, kc = i / kKB;
-        if ((j - kNQ) & 1) dp[kb] = mfma32x32x16(a, of[kc], dp[kb]);
-        else s[kb] = mfma32x32x16(a, qf[kc], s[kb]);
+  for (int j = 0; j < kRing; ++j) ring[j] = op(smem, smem, j);
+
+  f32x16 s[2], dp[2];
+  bf16x8 bs[4];      // bf16 dS^T of the four 16-key steps (B operands)
+  float de[16];      // dS of the half tile in progress
+
+  // P, dS of half tile b of the tile starting at key k0: element i holds key
+  // k0 + 32 b + 8 (i / 4) + 4 g + i % 4 of the lane's query
+  auto pds_elem = [&](int b, int i, int lim, auto mask_tag) __attribute__((always_inline)) {
+    float x = __builtin_fmaf(s[b][i], p.scale_log2, -lse2);
+    if (decltype(mask_tag)::value && 8 * (i >> 2) + (i & 3) > lim) x = kNegInf;
+    const float pv = exp2_hw(x);
+    de[i] = pv * (dp[b][i] - dval);
+    if ((i & 7) == 7) {
+      const int h = i - 7;
+      bs[2 * b + (i >> 3)] = pack_bf16x8(de[h], de[h + 1], de[h + 2], de[h + 3], de[h + 4], de[h + 5], de[h + 6],
+                                         de[h + 7]);
+      asm volatile("" ::"v"(bs[2 * b + (i >> 3)]));
+    }
+  };
+  // largest in-block key offset 8 (i / 4) + i % 4 that is visible to the lane
+  auto mask_lim = [&](int k0, int b) __attribute__((always_inline)) -> int {
+    const int last = CAUSAL ? (qi < p.Sk - 1 ? qi : p.Sk - 1) : p.Sk - 1;
+    return last - k0 - 32 * b - 4 * g;
+  };
+
+  // One tile.  FIRST: no previous half tile (its dQ products are skipped);
+  // MASK: mask this tile's elements; PMASK: the previous tile's.
+  auto tile = [&](int t, auto first_tag, auto mask_tag, auto pmask_tag, auto stage_tag)
+                  __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr int kS = decltype(stage_tag)::value;   // == t % kStages
+    const char* cur = smem + kS * L::kStageBytes;
+    const char* prev = smem + ((kS + kStages - 1) % kStages) * L::kStageBytes;
+    const char* nxt = smem + ((kS + 1) % kStages) * L::kStageBytes;
+    const int k0 = (n - 1 - t) * kBN;
+    const int lim0 = mask_lim(k0, 0);
+    const int plim1 = mask_lim(k0 + kBN, 1);
+
+    static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      constexpr int u = j / kU, jj = j % kU;
+      if constexpr (j == kBar) {
+        // every operand of the previous tile has been read; publish tile t + 1
+        if (t + 2 < n) wait_vmcnt<kPer>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 3 < n) issue(t + 3, std::integral_constant<int, (kS + 3) % kStages>{});
+      }
+      const bf16x8 a = ring[j % kRing];
+      if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, FIRST && j + kRing < kU ? cur : prev, j + kRing);
+      else ring[j % kRing] = op(nxt, cur, j + kRing - kSteps);
+      if constexpr (jj < kNS) {
+        // S^T (even), dP^T (odd) of half tile u, in VGPRs
+        if constexpr (jj < 2) {
+          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::init_v(dp[u], a, of[jj >> 1]);
+          else MfmaAsm<'v', 'a'>::init_v(s[u], a, qf[jj >> 1]);
+        } else {
+          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::acc_v(dp[u], a, of[jj >> 1]);
+          else MfmaAsm<'v', 'a'>::acc_v(s[u], a, qf[jj >> 1]);
+        }
+      } else if constexpr (!(FIRST && u == 0)) {
+        // dQ^T of the previous half tile: steps 2, 3 (u = 0, previous tile) or 0, 1
+        constexpr int qj = jj - kNS;
+        constexpr int ks = 2 * (1 - u) + qj / kDB, db = qj % kDB;
+        MfmaAsm<'v', 'v'>::acc_a(dq[db], a, bs[ks]);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto matrix = [&](int t, auto with_dq, auto with_s) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);
-    matrix_body(t, with_dq, with_s);
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // ---- vector phase: P^T and dS^T of tile t, packed to bf16
-  auto vector = [&](int t) __attribute__((always_inline)) {
-    if (t >= n_wave) return;
-    const int k0 = t * kBN;
-    const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = exp2_hw(__builtin_fmaf(s[kb][i], p.scale_log2, -lse2));
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= p.Sk || (CAUSAL && key > q_lane)) pv = 0.0f;
-        }
-        s[kb][i] = pv * (dp[kb][i] - dval);
+      // VALU during the S / dP products: P, dS of the previous half tile
+      if constexpr (jj < kNS && !(FIRST && u == 0)) {
+        constexpr int pb = 1 - u;   // its accumulators: block 1 (previous tile) or 0
+        if constexpr (jj == 0) mfma_drain_v2(s[pb], dp[pb]);
+        static_for<kPPS>([&](auto V) __attribute__((always_inline)) {
+          constexpr int i = jj * kPPS + V;
+          if constexpr (u == 0) pds_elem(pb, i, plim1, pmask_tag);
+          else pds_elem(pb, i, lim0, mask_tag);
+        });
       }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  using M = std::true_type;   // the two tiles next to the diagonal (or the ragged end) are masked
+  tile(0, T{}, M{}, F{}, S0{});
+  if (n > 1) tile(1, F{}, M{}, M{}, S1{});
+  int t = 2;
+  if (t < n) {
+    tile(t, F{}, F{}, M{}, S2{});   // its previous tile (1) was masked
+    ++t;
+    while (t < n) {
+      tile(t, F{}, F{}, F{}, S3{});
+      if (++t >= n) break;
+      tile(t, F{}, F{}, F{}, S0{});
+      if (++t >= n) break;
+      tile(t, F{}, F{}, F{}, S1{});
+      if (++t >= n) break;
+      tile(t, F{}, F{}, F{}, S2{});
+      ++t;
+    }
+  }
+
+  // ---- tail: P, dS and dQ^T of the last tile's half tile 1
+  {
+    const int tl = n - 1;
+    const char* last = smem + (tl % kStages) * L::kStageBytes;
+    const int k0 = (n - 1 - tl) * kBN;
+    const int plim = mask_lim(k0, 1);
+    mfma_drain_v2(s[1], dp[1]);
+    if (tl < 2) {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      const int kb = ks >> 1, h = (ks & 1) * 8;
-      pk[ks] = pack_bf16x8(s[kb][h], s[kb][h + 1], s[kb][h + 2], s[kb][h + 3], s[kb][h + 4], s[kb][h + 5],
-                           s[kb][h + 6], s[kb][h + 7]);
-    }
-  };
-
-  TileIO<D, kBN, kWaves> kio, vio;
-  auto fetch = [&](int u) __attribute__((always_inline)) {
-    if (u < n) {
-      kio.fetch(rk, u * kBN, wave, lane);
-      vio.fetch(rv, u * kBN, wave, lane);
-    }
-  };
-  auto commit = [&](int u) __attribute__((always_inline)) {
-    if (u < n) {
-      char* st = smem + (u % kStages) * L::kStageBytes;
-      kio.store(st, wave, lane);
-      vio.store(st + L::kTileBytes, wave, lane);
-    }
-  };
-  auto barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto m_s = [&](int t) __attribute__((always_inline)) { matrix(t, std::false_type{}, std::true_type{}); };
-  auto m_full = [&](int t) __attribute__((always_inline)) { matrix(t, std::true_type{}, std::true_type{}); };
-  auto m_dq = [&](int t) __attribute__((always_inline)) { matrix(t, std::true_type{}, std::false_type{}); };
-
-  fetch(0);
-  commit(0);
-  fetch(1);
-  commit(1);
-  barrier();
-
-  // Same interval schedule as the forward kernel: group 0 runs matrix(t) in
-  // interval 2t+1 and vector(t) in 2t+2; group 1 is one interval behind;
-  // tile u is fetched in interval 2u-3 and written at the end of 2u-2.
-  if (group == 0) {
-    fetch(2);
-    m_s(0);
-    barrier();
-    vector(0);
-    commit(2);
-    barrier();
-    for (int t = 1; t < n_wave; ++t) {
-      fetch(t + 2);
-      m_full(t);
-      barrier();
-      vector(t);
-      commit(t + 2);
-      barrier();
-    }
-    if (n_wave < n) {
-      fetch(n_wave + 2);
-      m_dq(n_wave);
-      barrier();
-      commit(n_wave + 2);
-      barrier();
-      for (int t = n_wave + 1; t < n; ++t) {
-        fetch(t + 2);
-        barrier();
-        commit(t + 2);
-        barrier();
-      }
-      barrier();
-      barrier();
+      for (int i = 0; i < 16; ++i) pds_elem(1, i, plim, T{});
     } else {
-      m_dq(n);
-      barrier();
-      barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pds_elem(1, i, plim, F{});
     }
-  } else {
-    fetch(2);
-    barrier();
-    m_s(0);
-    commit(2);
-    barrier();
-    fetch(3);
-    vector(0);
-    barrier();
-    for (int t = 1; t < n_wave; ++t) {
-      m_full(t);
-      commit(t + 2);
-      barrier();
-      fetch(t + 3);
-      vector(t);
-      barrier();
-    }
-    if (n_wave < n) {
-      m_dq(n_wave);
-      commit(n_wave + 2);
-      barrier();
-      fetch(n_wave + 3);
-      barrier();
-      for (int t = n_wave + 1; t < n; ++t) {
-        commit(t + 2);
-        barrier();
-        fetch(t + 3);
-        barrier();
-      }
-      barrier();
-    } else {
-      m_dq(n);
-      barrier();
+    asm volatile("s_nop 1" : "+v"(bs[2]), "+v"(bs[3]));   // VALU writes -> MFMA reads
+#pragma unroll
+    for (int qj = 0; qj < kNQ; ++qj) {
+      const int ks = 2 + qj / kDB, db = qj % kDB;
+      MfmaAsm<'v', 'v'>::acc_a(dq[db], read_cols<D>(last, tr_lane, ks, db), bs[ks]);
     }
   }
 
   // ---- dQ = scale (dQ^T)^T -> bf16 (lane = query, 4 consecutive dims per group)
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) mfma_drain_a(dq[db]);
   if (q_ok) {
-    bf16* row = p.dq + qi * D;
+    bf16* row = p.dq + ((size_t)bh * p.Sq + qi) * D;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -375,12 +382,6 @@ struct Layout {
   static constexpr int kLoadsPerTile = 2 * TileDMA<D, kBQ, kWaves>::kLoads + 1;   // per wave
 };
 }  // namespace kvk
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
