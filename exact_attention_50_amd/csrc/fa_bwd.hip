@@ -472,6 +472,23 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
         rrow, (__attribute__((address_space(3))) void*)(st + L::kRowsOff + wave * kBQ * 4), 4,
         (q0 + lane) * 4, 0, 0, 0);
   };
+  // load i (0 <= i < kPer) of relative tile t into stage S, issued one at a
+  // time so that the loads of a tile spread over several MFMA steps
+  auto issue_one = [&](int t, auto stage_tag, auto load_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(load_tag)::value;
+    constexpr int kL = TileDMA<D, kBQ, kWaves>::kLoads;
+    char* st = smem + decltype(stage_tag)::value * L::kStageBytes;
+    const int q0 = (qt_lo + t) * kBQ;
+    if constexpr (i < kL) {
+      TileDMA<D, kBQ, kWaves>::load_one(rq, q0, st, wave, lane, i);
+    } else if constexpr (i < 2 * kL) {
+      TileDMA<D, kBQ, kWaves>::load_one(rdo, q0, st + L::kTileBytes, wave, lane, i - kL);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rrow, (__attribute__((address_space(3))) void*)(st + L::kRowsOff + wave * kBQ * 4), 4,
+          (q0 + lane) * 4, 0, 0, 0);
+    }
+  };
 
   // operand j of a tile (j < 2 kNS: row reads of Q / dO for S / dP; then
   // transposed reads of dO / Q for dV / dK)
@@ -506,7 +523,13 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 
   // One tile; MASK: apply the causal mask (only the first kBK / kBQ tiles of
   // a causal key block hold keys after some of their rows).
-  auto tile = [&](int t, auto mask_tag, auto stage_tag) __attribute__((always_inline)) {
+  // A tile's kPer loads: the first kRing (or all) in the steps after the
+  // barrier of the tile three before it, the rest in the first steps of the
+  // tile two before it (FIRST: tile 0, whose "tile two ahead" was loaded by
+  // the prologue).
+  constexpr int kEarly = kPer < kRing ? kPer : kRing;
+  auto tile = [&](int t, auto first_tag, auto mask_tag, auto stage_tag) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int kS = decltype(stage_tag)::value;   // == t % kStages
     const char* cur = smem + kS * L::kStageBytes;
@@ -525,12 +548,20 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
       constexpr int j = J;
       if constexpr (j == kBar) {
         // every operand of tile t has been read; publish tile t + 1 (its
-        // loads were issued two tiles ago; those of t + 2 may still run)
+        // loads were all issued before tile t; the kPer loads of tile t + 2
+        // may still run)
         if (t + 2 < n) wait_vmcnt<kPer>();
         else wait_vmcnt<0>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 3 < n) issue(t + 3, stage_tag);
+      }
+      if constexpr (j >= kBar && j - kBar < kEarly) {
+        if (t + 3 < n) issue_one(t + 3, stage_tag, std::integral_constant<int, j - kBar>{});
+      }
+      if constexpr (!FIRST && j < kPer - kEarly) {
+        if (t + 2 < n)
+          issue_one(t + 2, std::integral_constant<int, (decltype(stage_tag)::value + 2) % kStages>{},
+                    std::integral_constant<int, kEarly + j>{});
       }
       const bf16x8 a = ring[j % kRing];
       if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, j + kRing);
@@ -596,15 +627,16 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   static_assert(kBK / kBQ == 2, "two masked tiles per causal key block");
   using M = std::integral_constant<bool, CAUSAL>;
   using F = std::false_type;
-  tile(0, M{}, S0{});
-  if (n > 1) tile(1, M{}, S1{});
+  using T = std::true_type;
+  tile(0, T{}, M{}, S0{});
+  if (n > 1) tile(1, F{}, M{}, S1{});
   int t = 2;
   while (t < n) {
-    tile(t, F{}, S2{});
+    tile(t, F{}, F{}, S2{});
     if (++t >= n) break;
-    tile(t, F{}, S0{});
+    tile(t, F{}, F{}, S0{});
     if (++t >= n) break;
-    tile(t, F{}, S1{});
+    tile(t, F{}, F{}, S1{});
     ++t;
   }
 

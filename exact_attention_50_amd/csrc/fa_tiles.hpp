@@ -112,18 +112,21 @@ struct TileDMA {
   static constexpr int kLoads = ROWS / TileGeom<D>::kRowsPerLoad / NW;
   static_assert(kLoads >= 1, "tile too small for the workgroup");
 
-  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
+  // load i (0 <= i < kLoads) of this wave
+  __device__ __forceinline__ static void load_one(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane,
+                                                  int i) {
     constexpr int RPL = TileGeom<D>::kRowsPerLoad;
     constexpr int C = TileGeom<D>::kChunks;
+    const int blk = i * NW + wave;   // wave-uniform
+    const int row = blk * RPL + lane / C;
+    const unsigned off = (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + ((lane % C) ^ tile_swz<D>(row)) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (__attribute__((address_space(3))) void*)(tile + blk * RPL * TileGeom<D>::kRowBytes), 16, (int)off, 0,
+        0, 0);
+  }
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int blk = i * NW + wave;   // wave-uniform
-      const int row = blk * RPL + lane / C;
-      const unsigned off = (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + ((lane % C) ^ tile_swz<D>(row)) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          src, (__attribute__((address_space(3))) void*)(tile + blk * RPL * TileGeom<D>::kRowBytes), 16,
-          (int)off, 0, 0, 0);
-    }
+    for (int i = 0; i < kLoads; ++i) load_one(src, row0, tile, wave, lane, i);
   }
 };
 

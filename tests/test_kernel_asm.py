@@ -72,26 +72,45 @@ def valu_def(ins):
     return regs(dst)
 
 
+BRANCH = re.compile(r"^s_(?:cbranch_\w+|branch)\s+(\S+)")
+
+
 def hazards(asm):
+    """VALU writes of an MFMA's source registers fewer than two wait states
+    before it, on any path into the MFMA (fall-through and branches)."""
     ins = instructions(asm)
+    preds = {}   # label -> indices of the branches that jump to it
+    for i, (text, is_label) in enumerate(ins):
+        m = None if is_label else BRANCH.match(text)
+        if m:
+            preds.setdefault(m.group(1), []).append(i)
     bad = []
+
+    def scan(j, budget, srcs, mfma, seen):
+        # walk back from instruction j with `budget` wait states left
+        while j >= 0 and budget > 0:
+            t, lab = ins[j]
+            if lab:
+                name = t.rstrip(":")
+                for bi in preds.get(name, []):
+                    if (bi, budget) not in seen:
+                        seen.add((bi, budget))
+                        scan(bi - 1, budget - 1, srcs, mfma, seen)   # the branch itself issues
+                j -= 1
+                if j >= 0 and not ins[j][1] and ins[j][0].startswith("s_branch"):
+                    return   # no fall-through into the label
+                continue
+            hit = valu_def(t) & srcs
+            if hit:
+                bad.append(f"{t}  ->  {mfma}")
+            budget -= wait_states(t)
+            j -= 1
+
     for i, (text, is_label) in enumerate(ins):
         if is_label or not text.startswith("v_mfma"):
             continue
         operands = text.split(None, 1)[1].split(",")
-        srcs = regs(",".join(operands[1:]))
-        ws, j = 0, i - 1
-        while j >= 0 and ws < 2:
-            t, lab = ins[j]
-            if lab:
-                break
-            hit = valu_def(t) & srcs
-            if hit:
-                bad.append(f"{t}  ->  {text}")
-            ws += wait_states(t)
-            j -= 1
-        if j >= 0 and ins[j][1] and ws < 2:
-            bad.append(f"block start {ins[j][0]} within two wait states of {text}")
+        scan(i - 1, 2, regs(",".join(operands[1:])), text, set())
     return bad
 
 
@@ -109,6 +128,17 @@ def test_scanner_finds_a_planted_hazard():
     """
     bad = hazards(snippet)
     assert len(bad) == 1 and "v_cvt_pk_bf16_f32 v3" in bad[0]
+    # a write on a branch path into the MFMA's block is found too
+    branchy = """
+    v_cvt_pk_bf16_f32 v7, v10, v11
+    s_cbranch_scc1 .LBB0_5
+    v_add_u32_e32 v40, v41, v42
+    s_nop 3
+    .LBB0_5:
+    v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[0:3], a[0:15]
+    """
+    bad = hazards(branchy)
+    assert len(bad) == 1 and "v_cvt_pk_bf16_f32 v7" in bad[0], bad
 
 
 @pytest.mark.parametrize("src", [s for s in build.sources() if s.endswith(("fa_bwd.hip", "fa_fwd.hip"))])
