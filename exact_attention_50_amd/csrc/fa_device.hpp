@@ -103,6 +103,14 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32)
 
 // max / sum of a value over the lane pair (l, l ^ 32), without LDS: after
 // v_permlane32_swap the two results hold x[l % 32] and x[l % 32 + 32].
+// max of three floats as one v_max3_f32 (no canonicalisation of the inputs;
+// the operands here are never signalling NaNs)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
                                                   false, false);

@@ -81,22 +81,24 @@ struct TileIO {
   static_assert(kLoads >= 1, "tile too small for the workgroup");
   u32x4 r[kLoads];
 
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane) {
+  __device__ __forceinline__ void fetch_one(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane, int i) {
     constexpr int RPL = TileGeom<D>::kRowsPerLoad;
+    const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
+    r[i] = load16(src, (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + (lane % TileGeom<D>::kChunks) * 16);
+  }
+  __device__ __forceinline__ void store_one(char* tile, int wave, int lane, int i) const {
+    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
+    const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
+    const int c = lane % TileGeom<D>::kChunks;
+    *reinterpret_cast<u32x4*>(tile + row * TileGeom<D>::kRowBytes + ((c ^ tile_swz<D>(row)) * 16)) = r[i];
+  }
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
-      r[i] = load16(src, (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + (lane % TileGeom<D>::kChunks) * 16);
-    }
+    for (int i = 0; i < kLoads; ++i) fetch_one(src, row0, wave, lane, i);
   }
   __device__ __forceinline__ void store(char* tile, int wave, int lane) const {
-    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
-      const int c = lane % TileGeom<D>::kChunks;
-      *reinterpret_cast<u32x4*>(tile + row * TileGeom<D>::kRowBytes + ((c ^ tile_swz<D>(row)) * 16)) = r[i];
-    }
+    for (int i = 0; i < kLoads; ++i) store_one(tile, wave, lane, i);
   }
 };
 

@@ -141,7 +141,22 @@ def test_scanner_finds_a_planted_hazard():
     assert len(bad) == 1 and "v_cvt_pk_bf16_f32 v7" in bad[0], bad
 
 
-@pytest.mark.parametrize("src", [s for s in build.sources() if s.endswith(("fa_bwd.hip", "fa_fwd.hip"))])
-def test_no_valu_write_right_before_mfma_read(src):
-    bad = hazards(assembly(src))
+KERNEL_SOURCES = [s for s in build.sources() if os.path.basename(s).startswith(("fa_bwd", "fa_fwd"))]
+
+
+@pytest.fixture(scope="module")
+def kernel_assembly():
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(KERNEL_SOURCES))) as ex:
+        return dict(zip(KERNEL_SOURCES, ex.map(assembly, KERNEL_SOURCES)))
+
+
+def test_kernel_sources_found():
+    names = {os.path.basename(s) for s in KERNEL_SOURCES}
+    assert "fa_bwd.hip" in names and any(n.startswith("fa_fwd") for n in names)
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES, ids=os.path.basename)
+def test_no_valu_write_right_before_mfma_read(src, kernel_assembly):
+    bad = hazards(kernel_assembly[src])
     assert not bad, "VALU write then MFMA read without two wait states:\n" + "\n".join(bad[:20])
