@@ -76,9 +76,9 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  * the arguments are invalid. */
 float fa_fwd_realised_emu_frac(int d, float emu_frac);
 
-/* Bytes of device workspace fa_bwd needs: the row terms
- * D_i = sum_c dO_ic O_ic, float32 [B,H,Sq] (rounded up to 256 bytes).
- * 0 on invalid sizes. */
+/* Bytes of device workspace fa_bwd needs: two float32 [B,H,Sq] arrays of
+ * row terms, D_i = sum_c dO_ic O_ic and LSE_i log2(e), each rounded up to
+ * 256 bytes.  0 on invalid sizes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic);
 
 /* Backward.  Q, K, V, O, dO bf16 and LSE float32 in (O and LSE as written
@@ -102,9 +102,10 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
 
 /* The three kernels of fa_bwd, enqueued separately (a bit mask, executed in
  * this order within one call):
- *   FA_BWD_PREPARE  D_i = sum_c dO_ic O_ic into the workspace;
- *   FA_BWD_DQ       dQ (reads D from the workspace; writes dQ only);
- *   FA_BWD_DKDV     dK and dV (reads D; writes dK, dV only).
+ *   FA_BWD_PREPARE  D_i = sum_c dO_ic O_ic and LSE_i log2(e) into the
+ *                   workspace;
+ *   FA_BWD_DQ       dQ (reads the row terms; writes dQ only);
+ *   FA_BWD_DKDV     dK and dV (reads the row terms; writes dK, dV only).
  * After PREPARE has completed, DQ and DKDV are independent and may run on
  * different streams (the caller orders them with events).  Arguments and
  * validation are those of fa_bwd; fa_bwd is fa_bwd_phase(FA_BWD_ALL, ...). */
