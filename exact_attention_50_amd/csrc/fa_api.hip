@@ -20,6 +20,13 @@ bool sizes_ok(int B, int H, int Sq, int Sk) {
 
 bool d_supported(int d) { return d == FA_D_SMALL || d == FA_D_LARGE; }
 
+// The kernels address one head of a tensor with 31-bit byte offsets and may
+// read up to a few tiles past its last row (those reads return zeros).
+bool head_addressable(int Sq, int Sk, int d) {
+  const long long rows = (Sq > Sk ? Sq : Sk) + 1024LL;
+  return rows * d * 2 < (1LL << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -50,6 +57,7 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
   if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdArgs a;
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
@@ -82,6 +90,7 @@ fa_status fa_bwd_phase(int phases, const void* Q, const void* K, const void* V, 
   if (deterministic != 0 && deterministic != 1) return FA_ERR_INVALID;
   if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
   if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa::bwd_workspace_bytes(B, H, Sq, Sk, d, deterministic != 0)) return FA_ERR_INVALID;
 
   fa::BwdArgs a;

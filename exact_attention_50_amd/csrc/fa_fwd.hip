@@ -12,7 +12,11 @@
 //
 // CDNA4 mapping (ours, not the pages'):
 //   * workgroup = 8 wavefronts x 32 query rows = 256 rows, one per CU; grid
-//     over (query block, head, batch), heaviest causal blocks first;
+//     over (query block, head, batch), heaviest causal blocks first.  A
+//     causal grid of fewer than two such blocks per CU is split instead:
+//     128-row workgroups whose two wave groups take alternate key tiles of
+//     the same rows and merge their partial (O, row sum, max) at the end, so
+//     heavy and light blocks can share the CUs;
 //   * ping-pong: waves 0-3 and 4-7 form two groups with one wave of each on
 //     every SIMD; the groups alternate between a matrix phase (O += V P of
 //     the previous tile, then S of the next tile) and a vector phase (the
@@ -70,7 +74,13 @@ struct FwdLayout {
 
 constexpr int kAhead = 6;   // MFMA operand fragments in flight per wave
 
-template <int D, bool CAUSAL, int EMU>
+// SPLIT (causal launches with few query blocks): a workgroup covers 128 rows
+// instead of 256; both wave groups hold the same rows, group g takes the key
+// tiles 2t + g, and group 1 hands its partial row state to group 0 at the
+// end.  Twice as many workgroups of half the size let the scheduler pair
+// heavy causal blocks with light ones when one 256-row block per CU would
+// leave the chip waiting on the heaviest.
+template <int D, bool CAUSAL, int EMU, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   using L = FwdLayout<D>;
   constexpr int kKB = kBN / 32;   // 32-key blocks per tile
@@ -98,7 +108,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
 
-  const int q_wave_lo = qb * kBM + wave * kQW;
+  constexpr int kRows = SPLIT ? kBM / 2 : kBM;   // query rows per workgroup
+  const int q_wave_lo = qb * kRows + (SPLIT ? (wave & 3) : wave) * kQW;
   const int q_lane = q_wave_lo + r32;
   const int k_lane = row_lane_offset<D>(lane);
   const int v_lane = tr_lane_offset<D>(lane);
@@ -109,10 +120,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   for (int kc = 0; kc < kKC; ++kc)
     qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, (unsigned)q_lane * L::kRowBytes + (kc * 16 + 8 * g) * 2));
 
-  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kRows) : p.Sk;
   const int n = (kv_end + kBN - 1) / kBN;
   // tiles this wave needs: causal stops at the wave's last row
   const int n_wave = CAUSAL ? min(n, (q_wave_lo + kQW - 1) / kBN + 1) : n;
+  // SPLIT: group g takes tiles 2t + g, all of them up to n: a causal tile
+  // past the wave's rows is fully masked (P = 0, the reference max stays).
+  // The waves move in step through the barriers and the last rows' waves
+  // set the pace, so such tiles cost no time, while a per-wave count would
+  // put a branch around the accumulating code, which the allocator answers
+  // with spills.  Group 1 with no tile (n = 1) still runs tile 1, whose keys
+  // all lie past Sk or past its rows.
+  int n_mine = SPLIT ? max(1, (n - group + 1) >> 1) : n_wave;
+  // hide the bound from the optimiser: knowing n_mine >= 1 it restructures
+  // the tile loop in a way that makes the allocator spill
+  if (SPLIT) asm volatile("" : "+s"(n_mine));
 
   f32x16 o[kDB];
 #pragma unroll
@@ -128,13 +150,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // them (which would not fit the register budget of two waves per SIMD).
   constexpr int kNV = kKS * kDB;    // P V products
   constexpr int kNK = kKB * kKC;    // K Q^T products
-  auto matrix_stream_body = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
+  // uk: the tile whose S is computed; uv: the tile whose P V is added
+  auto matrix_stream_body = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     constexpr bool SK = decltype(with_s)::value;
     constexpr int j0 = PV ? 0 : kNV;
     constexpr int j1 = SK ? kNV + kNK : kNV;
-    const char* vst = smem + ((t + kStages - 1) % kStages) * L::kStageBytes + L::kTileBytes;
-    const char* kst = smem + (t % kStages) * L::kStageBytes;
+    const char* vst = smem + (uv & (kStages - 1)) * L::kStageBytes + L::kTileBytes;
+    const char* kst = smem + (uk & (kStages - 1)) * L::kStageBytes;
     // j < kNV: (ks, db) = (j / kDB, j % kDB); j >= kNV: (kc, kb) = (i / kKB, i % kKB), i = j - kNV
     auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
       if (j < kNV) return read_cols<D>(vst, v_lane, j / kDB, j % kDB);
@@ -163,25 +186,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   };
   // The matrix phase runs at raised wave priority so its MFMAs issue ahead of
   // the vector-phase wave sharing the SIMD.
-  auto matrix_stream = [&](int t, auto with_pv, auto with_s) __attribute__((always_inline)) {
+  auto matrix_stream = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
-    matrix_stream_body(t, with_pv, with_s);
+    matrix_stream_body(uk, uv, with_pv, with_s);
     __builtin_amdgcn_s_setprio(0);
   };
+  // tiles of the group: consecutive (t) or every other one (SPLIT: 2t + group)
+  auto tile_of = [&](int t) __attribute__((always_inline)) -> int { return SPLIT ? 2 * t + group : t; };
   auto matrix_s = [&](int t) __attribute__((always_inline)) {
-    matrix_stream(t, std::false_type{}, std::true_type{});
+    matrix_stream(tile_of(t), 0, std::false_type{}, std::true_type{});
   };
   auto matrix_full = [&](int t) __attribute__((always_inline)) {
-    matrix_stream(t, std::true_type{}, std::true_type{});
+    matrix_stream(tile_of(t), tile_of(t - 1), std::true_type{}, std::true_type{});
   };
   auto matrix_pv = [&](int t) __attribute__((always_inline)) {
-    matrix_stream(t, std::true_type{}, std::false_type{});
+    matrix_stream(0, tile_of(t - 1), std::true_type{}, std::false_type{});
   };
 
   // ---- vector phase: softmax of tile t
   auto vector = [&](int t) __attribute__((always_inline)) {
-    if (t >= n_wave) return;
-    const int k0 = t * kBN;
+    if (t >= n_mine) return;
+    const int k0 = tile_of(t) * kBN;
     const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
     if (need_mask) {
 #pragma unroll
@@ -234,15 +259,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   };
 
   TileIO<D, kBN, kWaves> kio, vio;
+  // SPLIT fetches and writes unconditionally: past the last tile that costs
+  // a little bandwidth (rows past the head read as zeros) and saves the
+  // register copies a conditional load needs to keep the old contents.
   auto fetch = [&](int u) __attribute__((always_inline)) {
-    if (u < n) {
+    if (SPLIT || u < n) {
       kio.fetch(rk, u * kBN, wave, lane);
       vio.fetch(rv, u * kBN, wave, lane);
     }
   };
   auto commit = [&](int u) __attribute__((always_inline)) {
-    if (u < n) {
-      char* st = smem + (u % kStages) * L::kStageBytes;
+    if (SPLIT || u < n) {
+      char* st = smem + (u & (kStages - 1)) * L::kStageBytes;
       kio.store(st, wave, lane);
       vio.store(st + L::kTileBytes, wave, lane);
     }
@@ -253,94 +281,179 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  fetch(0);
-  commit(0);
-  fetch(1);
-  commit(1);
-  barrier();
-
-  // Phase schedule (interval k = 1 .. 2n+2, one workgroup barrier after each):
-  //   group 0: interval 2t+1 matrix(t), 2t+2 vector(t); 2n+1 matrix(n); 2n+2 idle
-  //   group 1: interval 1 idle; 2t+2 matrix(t), 2t+3 vector(t); 2n+2 matrix(n)
-  // matrix(t) = O += V_{t-1} P_{t-1} (t > 0) and S_t = K_t Q^T (t < n_wave);
-  // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
-  // n_wave - 1 but keeps taking part in the barriers.  Every wave fetches
-  // tile u into registers in interval 2u-3 and writes it to stage u % 4 at the
-  // end of interval 2u-2; tile u is read in intervals 2u+1 .. 2u+4.  Each
-  // variant of the matrix phase appears in a straight-line position of its
-  // own so the accumulators are never merged across branches.
-  if (group == 0) {
-    fetch(2);
-    matrix_s(0);
+  if constexpr (SPLIT) {
+    // Interval k = 1 .. max(n, 2) + 2, one workgroup barrier after each.  Every wave
+    // opens interval k by writing tile k (fetched during interval k-1) to
+    // stage k % 4 and fetching tile k+1, so tile u is readable from interval
+    // u+1.  Group g takes the tiles u = 2t + g: matrix(t) in interval 2t+1+g
+    // (S of tile u, P V of tile u-2) and vector(t) one interval later.  The
+    // last read of tile u (its V) falls in interval u+3, before tile u+4
+    // replaces it in interval u+4.
+    fetch(0);
+    commit(0);
+    fetch(1);
     barrier();
-    vector(0);
-    commit(2);
-    barrier();
-    for (int t = 1; t < n_wave; ++t) {
-      fetch(t + 2);
-      matrix_full(t);
+    int k = 1;
+    auto open = [&]() __attribute__((always_inline)) {
+      commit(k);
+      fetch(k + 1);
+    };
+    auto close = [&]() __attribute__((always_inline)) {
       barrier();
-      vector(t);
-      commit(t + 2);
-      barrier();
+      ++k;
+    };
+    if (group == 1) {
+      open();
+      close();
     }
-    if (n_wave < n) {
-      fetch(n_wave + 2);
-      matrix_pv(n_wave);
+    open();
+    matrix_s(0);
+    close();
+    open();
+    vector(0);
+    close();
+    for (int t = 1; t < n_mine; ++t) {
+      open();
+      matrix_full(t);
+      close();
+      open();
+      vector(t);
+      close();
+    }
+    open();
+    matrix_pv(n_mine);
+    close();
+    while (k <= max(n, 2) + 2) {
+      open();
+      close();
+    }
+  } else {
+    // Interval k = 1 .. 2n+2, one workgroup barrier after each:
+    //   group 0: interval 2t+1 matrix(t), 2t+2 vector(t); 2n+1 matrix(n); 2n+2 idle
+    //   group 1: interval 1 idle; 2t+2 matrix(t), 2t+3 vector(t); 2n+2 matrix(n)
+    // matrix(t) = O += V_{t-1} P_{t-1} (t > 0) and S_t = K_t Q^T (t < n_wave);
+    // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
+    // n_wave - 1 but keeps taking part in the barriers.  Every wave fetches
+    // tile u into registers in interval 2u-3 and writes it to stage u % 4 at
+    // the end of interval 2u-2; tile u is read in intervals 2u+1 .. 2u+4.
+    // Each variant of the matrix phase appears in a straight-line position
+    // of its own so the accumulators are never merged across branches.
+    fetch(0);
+    commit(0);
+    fetch(1);
+    commit(1);
+    barrier();
+    if (group == 0) {
+      fetch(2);
+      matrix_s(0);
       barrier();
-      commit(n_wave + 2);
+      vector(0);
+      commit(2);
       barrier();
-      for (int t = n_wave + 1; t < n; ++t) {
+      for (int t = 1; t < n_wave; ++t) {
         fetch(t + 2);
+        matrix_full(t);
         barrier();
+        vector(t);
         commit(t + 2);
         barrier();
       }
-      barrier();
-      barrier();
+      if (n_wave < n) {
+        fetch(n_wave + 2);
+        matrix_pv(n_wave);
+        barrier();
+        commit(n_wave + 2);
+        barrier();
+        for (int t = n_wave + 1; t < n; ++t) {
+          fetch(t + 2);
+          barrier();
+          commit(t + 2);
+          barrier();
+        }
+        barrier();
+        barrier();
+      } else {
+        matrix_pv(n);
+        barrier();
+        barrier();
+      }
     } else {
-      matrix_pv(n);
+      fetch(2);
       barrier();
+      matrix_s(0);
+      commit(2);
       barrier();
-    }
-  } else {
-    fetch(2);
-    barrier();
-    matrix_s(0);
-    commit(2);
-    barrier();
-    fetch(3);
-    vector(0);
-    barrier();
-    for (int t = 1; t < n_wave; ++t) {
-      matrix_full(t);
-      commit(t + 2);
+      fetch(3);
+      vector(0);
       barrier();
-      fetch(t + 3);
-      vector(t);
-      barrier();
-    }
-    if (n_wave < n) {
-      matrix_pv(n_wave);
-      commit(n_wave + 2);
-      barrier();
-      fetch(n_wave + 3);
-      barrier();
-      for (int t = n_wave + 1; t < n; ++t) {
+      for (int t = 1; t < n_wave; ++t) {
+        matrix_full(t);
         commit(t + 2);
         barrier();
         fetch(t + 3);
+        vector(t);
         barrier();
       }
-      barrier();
-    } else {
-      matrix_pv(n);
-      barrier();
+      if (n_wave < n) {
+        matrix_pv(n_wave);
+        commit(n_wave + 2);
+        barrier();
+        fetch(n_wave + 3);
+        barrier();
+        for (int t = n_wave + 1; t < n; ++t) {
+          commit(t + 2);
+          barrier();
+          fetch(t + 3);
+          barrier();
+        }
+        barrier();
+      } else {
+        matrix_pv(n);
+        barrier();
+      }
     }
   }
 
+  float l_lane = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
+  if constexpr (SPLIT) {
+    // group 1 hands (O, row sum, reference max) of each lane to the lane of
+    // group 0 that holds the same row and columns; the ring is idle now
+    constexpr int kXO = kDB * 4 * 256 * 16;   // O: [db * 4 + i4][256 lanes] f32x4
+    static_assert(kXO + 2 * 256 * 4 <= L::kLdsBytes, "merge area exceeds the LDS ring");
+    const int tl = (wave & 3) * 64 + lane;
+    f32x4* xo = reinterpret_cast<f32x4*>(smem);
+    float* xs = reinterpret_cast<float*>(smem + kXO);
+    if (group == 1) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          xo[(db * 4 + i4) * 256 + tl] = f32x4{o[db][4 * i4 + 0], o[db][4 * i4 + 1], o[db][4 * i4 + 2],
+                                               o[db][4 * i4 + 3]};
+      xs[tl] = m_ref;
+      xs[256 + tl] = l_lane;
+    }
+    barrier();
+    if (group == 1) return;
+    const float m1 = xs[tl];
+    const float m = __builtin_fmaxf(m_ref, m1);
+    // a group that saw no key of this row has m = -inf and weight 0
+    const float a0 = (m_ref == kNegInf) ? 0.0f : exp2_hw(m_ref - m);
+    const float a1 = (m1 == kNegInf) ? 0.0f : exp2_hw(m1 - m);
+    l_lane = l_lane * a0 + xs[256 + tl] * a1;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 x = xo[(db * 4 + i4) * 256 + tl];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[db][4 * i4 + c] = o[db][4 * i4 + c] * a0 + x[c] * a1;
+      }
+    m_ref = m;
+  }
+
   // ---- epilogue: O = O / l (bf16), LSE = (m_ref + log2 l) ln 2
-  const float l = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+  const float l = pair_sum(l_lane);
   const float inv_l = 1.0f / l;
   if (q_lane < p.Sq) {
     bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
@@ -359,9 +472,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 // Software-exponential counts per lane per tile that are instantiated.
 constexpr int kEmuCounts[] = {0, 3, 8, 16, 32};
 
-template <int D, bool CAUSAL, int EMU>
+template <int D, bool CAUSAL, int EMU, bool SPLIT>
 hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
-  auto kern = fwd_kernel<D, CAUSAL, EMU>;
+  auto kern = fwd_kernel<D, CAUSAL, EMU, SPLIT>;
   const int lds = FwdLayout<D>::kLdsBytes;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -370,17 +483,23 @@ hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_d_causal(const FwdParams& prm, int emu, dim3 grid, hipStream_t stream) {
   switch (emu) {
-    case 0: return launch_one<D, CAUSAL, 0>(prm, grid, stream);
-    case 3: return launch_one<D, CAUSAL, 3>(prm, grid, stream);
-    case 8: return launch_one<D, CAUSAL, 8>(prm, grid, stream);
-    case 16: return launch_one<D, CAUSAL, 16>(prm, grid, stream);
-    case 32: return launch_one<D, CAUSAL, 32>(prm, grid, stream);
+    case 0: return launch_one<D, CAUSAL, 0, SPLIT>(prm, grid, stream);
+    case 3: return launch_one<D, CAUSAL, 3, SPLIT>(prm, grid, stream);
+    case 8: return launch_one<D, CAUSAL, 8, SPLIT>(prm, grid, stream);
+    case 16: return launch_one<D, CAUSAL, 16, SPLIT>(prm, grid, stream);
+    case 32: return launch_one<D, CAUSAL, 32, SPLIT>(prm, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
+
+// Causal launches split a query block over both wave groups when the grid
+// of 256-row blocks would give fewer than two workgroups per CU: a workgroup
+// fills a CU, so with one wave of workgroups the heaviest block sets the
+// time, while 128-row blocks of half the cost can be paired heavy with light.
+constexpr int kSplitBelowBlocks = 512;
 
 }  // namespace
 
@@ -405,16 +524,21 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   prm.BH = a.B * a.H;
   prm.Sq = a.Sq;
   prm.Sk = a.Sk;
-  prm.n_qblocks = (a.Sq + kBM - 1) / kBM;
   prm.scale_log2 = a.scale * kLog2e;
   prm.tau = a.tau;
+  const long long full_blocks = (long long)((a.Sq + kBM - 1) / kBM) * prm.BH;
+  const bool split = a.causal && full_blocks < kSplitBelowBlocks;
+  const int rows = split ? kBM / 2 : kBM;
+  prm.n_qblocks = (a.Sq + rows - 1) / rows;
   const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
   if (a.d == 64) {
-    return a.causal ? launch_d_causal<64, true>(prm, a.emu_count, grid, stream)
-                    : launch_d_causal<64, false>(prm, a.emu_count, grid, stream);
+    if (!a.causal) return launch_d_causal<64, false, false>(prm, a.emu_count, grid, stream);
+    return split ? launch_d_causal<64, true, true>(prm, a.emu_count, grid, stream)
+                 : launch_d_causal<64, true, false>(prm, a.emu_count, grid, stream);
   }
-  return a.causal ? launch_d_causal<128, true>(prm, a.emu_count, grid, stream)
-                  : launch_d_causal<128, false>(prm, a.emu_count, grid, stream);
+  if (!a.causal) return launch_d_causal<128, false, false>(prm, a.emu_count, grid, stream);
+  return split ? launch_d_causal<128, true, true>(prm, a.emu_count, grid, stream)
+               : launch_d_causal<128, true, false>(prm, a.emu_count, grid, stream);
 }
 
 // ---------------------------------------------------------------- exp2 probe

@@ -44,11 +44,15 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID = 1,      /* null pointer, bad size, bad scalar, misaligned pointer, small workspace */
-  FA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (d, causal Sq != Sk) */
+  FA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (d, causal Sq != Sk,
+                              a head longer than the limit below) */
   FA_ERR_HIP = 3           /* the HIP runtime reported an error while launching */
 } fa_status;
 
-/* Head dimensions the kernels are built for. */
+/* Head dimensions the kernels are built for.  One head of any tensor must
+ * be addressable with 31-bit byte offsets: (max(Sq, Sk) + 1024) * d * 2 <
+ * 2^31, i.e. up to about 8.4 M rows at d = 128; longer heads return
+ * FA_ERR_UNSUPPORTED. */
 #define FA_D_SMALL 64
 #define FA_D_LARGE 128
 

@@ -53,6 +53,8 @@ def _fwd(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=16, d=
     (dict(scale=float("nan")), fa.FA_ERR_INVALID), (dict(tau=-1.0), fa.FA_ERR_INVALID),
     (dict(tau=65.0), fa.FA_ERR_INVALID), (dict(emu=1.5), fa.FA_ERR_INVALID), (dict(causal=2), fa.FA_ERR_INVALID),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=32), fa.FA_ERR_UNSUPPORTED),
+    # one head past 31-bit byte offsets: (8M + 1024) rows x 128 dims x 2 bytes
+    (dict(d=128, Sq=16, Sk=(1 << 23)), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects_before_any_launch(L, kw, status):
     assert _fwd(L, **kw) == status
