@@ -72,7 +72,7 @@ struct FwdLayout {
   static constexpr int kLdsBytes = kStages * kStageBytes;
 };
 
-constexpr int kAhead = 6;   // MFMA operand fragments in flight per wave
+constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
 
 // SPLIT (causal launches with few query blocks): a workgroup covers 128 rows
 // instead of 256; both wave groups hold the same rows, group g takes the key
