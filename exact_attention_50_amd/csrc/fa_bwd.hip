@@ -468,9 +468,7 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     const int q0 = (qt_lo + t) * kBQ;
     TileDMA<D, kBQ, kWaves>::load(rq, q0, st, wave, lane);
     TileDMA<D, kBQ, kWaves>::load(rdo, q0, st + L::kTileBytes, wave, lane);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rrow, (__attribute__((address_space(3))) void*)(st + L::kRowsOff + wave * kBQ * 4), 4,
-        (q0 + lane) * 4, 0, 0, 0);
+    lds_dma4(rrow, (unsigned)(q0 + lane) * 4, st + L::kRowsOff + wave * kBQ * 4);
   };
   // load i (0 <= i < kPer) of relative tile t into stage S, issued one at a
   // time so that the loads of a tile spread over several MFMA steps
@@ -484,9 +482,7 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     } else if constexpr (i < 2 * kL) {
       TileDMA<D, kBQ, kWaves>::load_one(rdo, q0, st + L::kTileBytes, wave, lane, i - kL);
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rrow, (__attribute__((address_space(3))) void*)(st + L::kRowsOff + wave * kBQ * 4), 4,
-          (q0 + lane) * 4, 0, 0, 0);
+      lds_dma4(rrow, (unsigned)(q0 + lane) * 4, st + L::kRowsOff + wave * kBQ * 4);
     }
   };
 

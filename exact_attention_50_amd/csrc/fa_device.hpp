@@ -156,6 +156,27 @@ __device__ __forceinline__ void static_for(F&& f) {
 // prefetches stay in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Memory-to-LDS loads (buffer_load ... lds) written out as instructions.
+// Lane i's bytes land at the LDS address in M0 plus 4 i (dword) or 16 i
+// (dwordx4); M0 must be wave-uniform.  The compiler's own form of these loads
+// makes it wait for every outstanding vector-memory load before any later
+// LDS read that it cannot prove disjoint from the load's target, which in a
+// ring of stages is every read, and so throws away the lead the loads were
+// issued with.  Callers order the loads themselves: s_waitcnt vmcnt, then a
+// barrier, before any wave reads what they wrote.  The s_nop is the wait
+// state required between the write of M0 and its use by the load.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned voffset, const void* lds_dst) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(r), "{m0}"(lds_addr(lds_dst)) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, unsigned voffset, const void* lds_dst) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(r), "{m0}"(lds_addr(lds_dst)) : "memory");
+}
+
 // Workgroup barrier that also waits for this wave's memory-to-LDS loads (and
 // every other vector-memory load of the wave).
 __device__ __forceinline__ void dma_barrier() {

@@ -31,9 +31,10 @@
 //     operand (keys of each 16-key group in a fixed permuted order); the V^T
 //     A operand is read from row-major V in LDS with ds_read_b64_tr_b16;
 //   * K / V tiles: 4-stage LDS ring with the chunk permutation of
-//     fa_tiles.hpp (bank-conflict-free operand reads); each tile is fetched
-//     to registers one matrix phase ahead and written to LDS one phase later;
-//     buffer descriptors bound every head, so rows past the end read zeros.
+//     fa_tiles.hpp (bank-conflict-free operand reads), loaded memory-to-LDS
+//     about three phases ahead of their first read (the split form stages
+//     them through registers instead); buffer descriptors bound every head,
+//     so rows past the end read zeros.
 
 #include <type_traits>
 
@@ -258,21 +259,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
+  // Tile IO.  The 256-row form loads each K/V tile straight into its LDS
+  // stage (memory-to-LDS loads, no registers): tile u is issued where
+  // fetch(u) stands, in interval 2u-3, once its stage's previous tile (u-4)
+  // has been read for the last time, and commit(u), at the end of interval
+  // 2u-2, only waits for the tile before it (u-1, first read in interval
+  // 2u-1), so every tile has about three intervals to arrive.  The split
+  // form writes tile k+1's stage in the interval right after tile k-3's last
+  // read; it stages tiles through registers (fetch one interval ahead, write
+  // to LDS at the start of the next), so the global load gets a whole
+  // interval without a fifth stage.  It fetches and writes unconditionally:
+  // past the last tile that costs a little bandwidth (rows past the head
+  // read as zeros) and saves the register copies a conditional load needs.
   TileIO<D, kBN, kWaves> kio, vio;
-  // SPLIT fetches and writes unconditionally: past the last tile that costs
-  // a little bandwidth (rows past the head read as zeros) and saves the
-  // register copies a conditional load needs to keep the old contents.
+  constexpr int kDmaPerTile = 2 * TileDMA<D, kBN, kWaves>::kLoads;   // per wave
   auto fetch = [&](int u) __attribute__((always_inline)) {
-    if (SPLIT || u < n) {
+    if constexpr (SPLIT) {
       kio.fetch(rk, u * kBN, wave, lane);
       vio.fetch(rv, u * kBN, wave, lane);
+    } else if (u < n) {
+      char* st = smem + (u & (kStages - 1)) * L::kStageBytes;
+      TileDMA<D, kBN, kWaves>::load(rk, u * kBN, st, wave, lane);
+      TileDMA<D, kBN, kWaves>::load(rv, u * kBN, st + L::kTileBytes, wave, lane);
     }
   };
   auto commit = [&](int u) __attribute__((always_inline)) {
-    if (SPLIT || u < n) {
+    if constexpr (SPLIT) {
       char* st = smem + (u & (kStages - 1)) * L::kStageBytes;
       kio.store(st, wave, lane);
       vio.store(st + L::kTileBytes, wave, lane);
+    } else if (u < n) {
+      // tile u's loads are the newest; everything older is complete
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerTile) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
   auto barrier = [&]() __attribute__((always_inline)) {
@@ -333,11 +353,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     //   group 1: interval 1 idle; 2t+2 matrix(t), 2t+3 vector(t); 2n+2 matrix(n)
     // matrix(t) = O += V_{t-1} P_{t-1} (t > 0) and S_t = K_t Q^T (t < n_wave);
     // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
-    // n_wave - 1 but keeps taking part in the barriers.  Every wave fetches
-    // tile u into registers in interval 2u-3 and writes it to stage u % 4 at
-    // the end of interval 2u-2; tile u is read in intervals 2u+1 .. 2u+4.
-    // Each variant of the matrix phase appears in a straight-line position
-    // of its own so the accumulators are never merged across branches.
+    // n_wave - 1 but keeps taking part in the barriers.  Every wave issues
+    // its loads of tile u into stage u % 4 in interval 2u-3 (fetch) and
+    // waits for those of tile u-1 at the end of interval 2u-2 (commit);
+    // tile u is read in intervals 2u+1 .. 2u+4.  Each variant of the matrix
+    // phase appears in a straight-line position of its own so the
+    // accumulators are never merged across branches.  Prologue: after
+    // commit(1) (which waits for tile 0) and the barrier, tile 0 is readable.
     fetch(0);
     commit(0);
     fetch(1);

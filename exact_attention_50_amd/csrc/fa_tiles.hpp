@@ -122,9 +122,7 @@ struct TileDMA {
     const int blk = i * NW + wave;   // wave-uniform
     const int row = blk * RPL + lane / C;
     const unsigned off = (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + ((lane % C) ^ tile_swz<D>(row)) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (__attribute__((address_space(3))) void*)(tile + blk * RPL * TileGeom<D>::kRowBytes), 16, (int)off, 0,
-        0, 0);
+    lds_dma16(src, off, tile + blk * RPL * TileGeom<D>::kRowBytes);
   }
   __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
 #pragma unroll
