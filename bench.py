@@ -256,6 +256,35 @@ def main():
                     "emu_realised": round(fa.fa_fwd_realised_emu_frac(ww.d, emu), 4)}
             del del_ins, qq, kk, vv, oo, ll
 
+        # split-KV: the causal S=8192 workload as 4 key ranges (fa_fwd_partial
+        # into float32 parts) plus fa_merge; the merge is HBM-bound
+        ww = WORKLOADS[3]
+        qq, kk, vv = [t.to(dev) for t in workload_inputs(ww)][:3]
+        n_parts = 4
+        bounds = [ww.Sk * i // n_parts for i in range(n_parts + 1)]
+        op = torch.empty((n_parts,) + tuple(qq.shape), dtype=torch.float32, device=dev)
+        lp = torch.empty((n_parts,) + tuple(qq.shape[:3]), dtype=torch.float32, device=dev)
+        om = torch.empty_like(qq)
+        lm = torch.empty(qq.shape[:3], dtype=torch.float32, device=dev)
+
+        def partials():
+            for i in range(n_parts):
+                fa.fa_fwd_partial(qq, kk, vv, op[i], lp[i], 0, bounds[i], bounds[i + 1], causal=True,
+                                  scale=ww.scale, tau=args.tau)
+
+        ms_p = time_calls(partials, max(10, args.steps), 3)
+        ms_m = time_calls(lambda: fa.fa_merge(op, lp, om, lm), max(10, args.steps), 3)
+        rows = ww.B * ww.H * ww.Sq
+        merge_bytes = n_parts * rows * (ww.d * 4 + 4) + rows * (ww.d * 2 + 4)
+        gbs = merge_bytes / (ms_m * 1e-3) / 1e9
+        extra["split_kv"] = {
+            "workload": f"{ww.name} as {n_parts} key ranges + merge",
+            "partials_ms": round(ms_p, 5), "merge_ms": round(ms_m, 5),
+            "tflops": round(ww.flops("fwd") / ((ms_p + ms_m) * 1e-3) / 1e12, 2),
+            "merge_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": merge_bytes}}
+        del qq, kk, vv, op, lp, om, lm
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)

@@ -14,8 +14,9 @@ import math
 import os
 
 __all__ = [
-    "FAError", "lib", "fa_fwd", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes", "fa_exp2_probe",
-    "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "backward", "LIB_PATH",
+    "FAError", "lib", "fa_fwd", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
+    "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
+    "backward", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -44,6 +45,10 @@ def lib():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
+    L.fa_fwd_partial.restype = i
+    L.fa_merge.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
+    L.fa_merge.restype = i
     L.fa_fwd_realised_emu_frac.argtypes = [i, f]
     L.fa_fwd_realised_emu_frac.restype = f
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -113,6 +118,39 @@ def fa_fwd(q, k, v, o, lse, causal=False, scale=None, tau=8.0, emu_frac=0.0):
         raise FAError(st, "fa_fwd")
 
 
+def fa_fwd_partial(q, k, v, o_part, lse_part, q_offset, k_begin, k_end, causal=False, scale=None, tau=8.0,
+                   emu_frac=0.0):
+    """Enqueue the forward over keys k_begin..k_end-1; fills the float32
+    o_part [B,H,Sq,d] and lse_part [B,H,Sq] in place."""
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    _check_bf16("q", q, (B, H, Sq, d))
+    _check_bf16("k", k, (B, H, Sk, d))
+    _check_bf16("v", v, (B, H, Sk, d))
+    _check_f32("o_part", o_part, (B, H, Sq, d))
+    _check_f32("lse_part", lse_part, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, H, Sq, Sk, d,
+                              int(q_offset), int(k_begin), int(k_end), int(bool(causal)), float(scale), float(tau),
+                              float(emu_frac), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_partial")
+
+
+def fa_merge(o_parts, lse_parts, o, lse):
+    """Enqueue the merge of n partial results: o_parts float32 [n,B,H,Sq,d],
+    lse_parts float32 [n,B,H,Sq]; fills the bf16 o and float32 lse."""
+    n, B, H, Sq, d = o_parts.shape
+    _check_f32("o_parts", o_parts, (n, B, H, Sq, d))
+    _check_f32("lse_parts", lse_parts, (n, B, H, Sq))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    st = lib().fa_merge(_ptr(o_parts), _ptr(lse_parts), n, B, H, Sq, d, _ptr(o), _ptr(lse), _stream(o))
+    if st != FA_OK:
+        raise FAError(st, "fa_merge")
+
+
 def fa_bwd_phase(phases, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None,
                  deterministic=False):
     """Enqueue the backward kernels selected by the FA_BWD_* bit mask."""
@@ -170,6 +208,26 @@ def forward(q, k, v, causal=False, scale=None, tau=8.0, emu_frac=0.0):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, causal=causal, scale=scale, tau=tau, emu_frac=emu_frac)
+    return o, lse
+
+
+def forward_partial(q, k, v, q_offset, k_begin, k_end, causal=False, scale=None, tau=8.0, emu_frac=0.0):
+    """Returns (O_part float32 [B,H,Sq,d], LSE_part float32 [B,H,Sq])."""
+    import torch
+    B, H, Sq, d = q.shape
+    o = torch.empty((B, H, Sq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    fa_fwd_partial(q, k, v, o, lse, q_offset, k_begin, k_end, causal=causal, scale=scale, tau=tau, emu_frac=emu_frac)
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq])."""
+    import torch
+    n, B, H, Sq, d = o_parts.shape
+    o = torch.empty((B, H, Sq, d), dtype=torch.bfloat16, device=o_parts.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=o_parts.device)
+    fa_merge(o_parts, lse_parts, o, lse)
     return o, lse
 
 

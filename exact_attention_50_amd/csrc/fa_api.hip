@@ -62,11 +62,52 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   fa::FwdArgs a;
   a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.q_off = 0; a.k_begin = 0; a.k_end = Sk;
   a.causal = causal != 0;
   a.scale = scale;
   a.tau = tau;
   a.emu_count = fa::fwd_nearest_emu_count(d, emu_frac);
   const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_partial(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part, int B, int H,
+                         int Sq, int Sk, int d, int q_offset, int k_begin, int k_end, int causal, float scale,
+                         float tau, float emu_frac, void* stream) {
+  if (!Q || !K || !V || !O_part || !LSE_part) return FA_ERR_INVALID;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O_part) || !aligned16(LSE_part))
+    return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (q_offset < 0 || k_begin < 0 || k_end <= k_begin || k_end > Sk) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 64.0f)) return FA_ERR_INVALID;
+  if (!(emu_frac >= 0.0f && emu_frac <= 1.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+  if ((long long)q_offset + Sq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = nullptr; a.o32 = O_part; a.lse = LSE_part;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.q_off = q_offset; a.k_begin = k_begin; a.k_end = k_end;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.tau = tau;
+  a.emu_count = fa::fwd_nearest_emu_count(d, emu_frac);
+  const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_merge(const float* O_parts, const float* LSE_parts, int n_parts, int B, int H, int Sq, int d, void* O,
+                   float* LSE, void* stream) {
+  if (!O_parts || !LSE_parts || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(O_parts) || !aligned16(LSE_parts) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  if (n_parts < 1 || !sizes_ok(B, H, Sq, Sq)) return FA_ERR_INVALID;
+  if ((long long)n_parts * B * H * Sq >= (1LL << 31)) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  const hipError_t e = fa::launch_merge(O_parts, LSE_parts, n_parts, B * H * Sq, d, O, LSE,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

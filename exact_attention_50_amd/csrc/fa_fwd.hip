@@ -56,10 +56,14 @@ struct FwdParams {
   const bf16* q;
   const bf16* k;
   const bf16* v;
-  bf16* o;
+  bf16* o;           // bf16 output, or
+  float* o32;        // float32 output when non-null
   float* lse;
   int BH;            // B * H
-  int Sq, Sk;
+  int Sq, Sk;        // rows per head of Q / O and of K / V
+  int k_begin;       // the keys attended to: k_begin .. k_begin + k_len - 1
+  int k_len;
+  int q_off;         // global index of query row 0 (causal: key j visible iff k_begin + j <= q_off + i)
   int n_qblocks;
   float scale_log2;  // scale * log2(e)
   float tau;
@@ -103,11 +107,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const int bh = blockIdx.x % p.BH;
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
 
+  // key indices below are local to the range (key j is global key k_begin + j)
   const unsigned head_q = (unsigned)p.Sq * L::kRowBytes;
-  const unsigned head_k = (unsigned)p.Sk * L::kRowBytes;
+  const unsigned head_k = (unsigned)p.k_len * L::kRowBytes;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * D, head_q);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + ((size_t)bh * p.Sk + p.k_begin) * D, head_k);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + ((size_t)bh * p.Sk + p.k_begin) * D, head_k);
 
   constexpr int kRows = SPLIT ? kBM / 2 : kBM;   // query rows per workgroup
   const int q_wave_lo = qb * kRows + (SPLIT ? (wave & 3) : wave) * kQW;
@@ -121,10 +126,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   for (int kc = 0; kc < kKC; ++kc)
     qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, (unsigned)q_lane * L::kRowBytes + (kc * 16 + 8 * g) * 2));
 
-  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kRows) : p.Sk;
+  // causal, in local key coordinates: row i sees keys j <= i + q_diag
+  const int q_diag = p.q_off - p.k_begin;
+  const int kv_end = CAUSAL ? min(p.k_len, q_diag + (qb + 1) * kRows) : p.k_len;
+  if (kv_end <= 0) {
+    // no key is visible to any row of the block (key range after its rows)
+    if (!(SPLIT && group == 1) && q_lane < p.Sq) {
+      if (p.o32) {
+        float* orow = p.o32 + ((size_t)bh * p.Sq + q_lane) * D;
+#pragma unroll
+        for (int c = 0; c < D / 2; c += 4) *reinterpret_cast<f32x4*>(orow + c + (D / 2) * g) = f32x4{};
+      } else {
+        bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
+#pragma unroll
+        for (int c = 0; c < D / 2; c += 8) *reinterpret_cast<u32x4*>(orow + c + (D / 2) * g) = u32x4{};
+      }
+      if (g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = kNegInf;
+    }
+    return;
+  }
   const int n = (kv_end + kBN - 1) / kBN;
-  // tiles this wave needs: causal stops at the wave's last row
-  const int n_wave = CAUSAL ? min(n, (q_wave_lo + kQW - 1) / kBN + 1) : n;
+  // tiles this wave needs: causal stops at the wave's last row; a wave whose
+  // rows see no key of the range still runs tile 0, fully masked
+  int n_wave = CAUSAL ? max(1, min(n, (q_diag + q_wave_lo + kQW + kBN - 1) / kBN)) : n;
+  // as for n_mine below: knowing the bound, the optimiser reshapes the tile
+  // loops in a way that makes the allocator spill
+  if (CAUSAL) asm volatile("" : "+s"(n_wave));
   // SPLIT: group g takes tiles 2t + g, all of them up to n: a causal tile
   // past the wave's rows is fully masked (P = 0, the reference max stays).
   // The waves move in step through the barriers and the last rows' waves
@@ -208,14 +235,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   auto vector = [&](int t) __attribute__((always_inline)) {
     if (t >= n_mine) return;
     const int k0 = tile_of(t) * kBN;
-    const bool need_mask = (k0 + kBN > p.Sk) || (CAUSAL && k0 + kBN - 1 > q_wave_lo);
+    const bool need_mask = (k0 + kBN > p.k_len) || (CAUSAL && k0 + kBN - 1 > q_diag + q_wave_lo);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= p.Sk || (CAUSAL && key > q_lane)) s[kb][i] = kNegInf;
+          if (key >= p.k_len || (CAUSAL && key > q_diag + q_lane)) s[kb][i] = kNegInf;
         }
     }
     // row max: 8 independent chains, then a short tree
@@ -474,20 +501,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     m_ref = m;
   }
 
-  // ---- epilogue: O = O / l (bf16), LSE = (m_ref + log2 l) ln 2
+  // ---- epilogue: O = O / l (bf16 or float32), LSE = (m_ref + log2 l) ln 2;
+  // a row that saw no key (only possible for a key range) gets O = 0 and
+  // LSE = -inf, the identity of the merge of partial results
   const float l = pair_sum(l_lane);
-  const float inv_l = 1.0f / l;
+  const bool empty = !(l > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l;
   if (q_lane < p.Sq) {
-    bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
+    if (p.o32) {
+      float* orow = p.o32 + ((size_t)bh * p.Sq + q_lane) * D;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+      for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = {o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
-                          o[db][4 * i4 + 3] * inv_l};
-        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
-      }
-    if (g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = (m_ref + __builtin_log2f(l)) * kLn2;
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) =
+              f32x4{o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
+                    o[db][4 * i4 + 3] * inv_l};
+    } else {
+      bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v4 = {o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
+                            o[db][4 * i4 + 3] * inv_l};
+          *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
+        }
+    }
+    if (g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = empty ? kNegInf : (m_ref + __builtin_log2f(l)) * kLn2;
   }
 }
 
@@ -542,10 +583,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   prm.k = static_cast<const bf16*>(a.k);
   prm.v = static_cast<const bf16*>(a.v);
   prm.o = static_cast<bf16*>(a.o);
+  prm.o32 = a.o32;
   prm.lse = a.lse;
   prm.BH = a.B * a.H;
   prm.Sq = a.Sq;
   prm.Sk = a.Sk;
+  prm.k_begin = a.k_begin;
+  prm.k_len = a.k_end - a.k_begin;
+  prm.q_off = a.q_off;
   prm.scale_log2 = a.scale * kLog2e;
   prm.tau = a.tau;
   const long long full_blocks = (long long)((a.Sq + kBM - 1) / kBM) * prm.BH;

@@ -10,9 +10,13 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  void* o;
+  void* o;               // bf16 output, used when o32 is null
+  float* o32 = nullptr;  // float32 output
   float* lse;
   int B, H, Sq, Sk, d;
+  int q_off = 0;         // global index of query row 0
+  int k_begin = 0;       // keys k_begin .. k_end - 1 are attended to
+  int k_end = 0;
   bool causal;
   float scale;
   float tau;
@@ -25,6 +29,10 @@ int fwd_exps_per_lane_tile(int d);
 int fwd_nearest_emu_count(int d, float emu_frac);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// rows = B * H * Sq; parts are n_parts consecutive [rows, d] / [rows] arrays
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int d, void* o,
+                        float* lse, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

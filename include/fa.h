@@ -75,6 +75,39 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
                  int B, int H, int Sq, int Sk, int d, int causal, float scale,
                  float tau, float emu_frac, void* stream);
 
+/* Forward over a range of keys, for split-KV and ring (context-parallel)
+ * attention: queries i = 0 .. Sq-1 of Q (global index q_offset + i) attend to
+ * the keys j = k_begin .. k_end-1 of K, V only (causal: key j is visible iff
+ * j <= q_offset + i).  Writes, per row, the output normalised over those keys
+ * alone, O_part = softmax(scale q K_r^T) V_r (float32 [B,H,Sq,d]), and the
+ * log-sum-exp of its scores, LSE_part (float32 [B,H,Sq], natural log).  A row
+ * that sees no key of the range gets O_part = 0 and LSE_part = -inf.  The
+ * method is fa_fwd's (online softmax with conditional rescale, software 2^x
+ * share); fa_merge combines parts over disjoint ranges into the result over
+ * their union.  This is the single-GPU piece of the fused ring attention
+ * that the lecture notes "How FlashAttention 4 Works" list among the open
+ * directions for multi-GPU FA4 (their closing list of what comes next).
+ *   Q is [B,H,Sq,d], K and V are [B,H,Sk,d] (all heads' full key arrays; the
+ *   range selects rows inside each head).
+ *   0 <= k_begin < k_end <= Sk; q_offset >= 0; causal 0 or 1 (Sq != Sk is
+ *   allowed); other arguments as for fa_fwd.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+fa_status fa_fwd_partial(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part,
+                         int B, int H, int Sq, int Sk, int d, int q_offset, int k_begin, int k_end,
+                         int causal, float scale, float tau, float emu_frac, void* stream);
+
+/* Merge of n_parts partial results (as written by fa_fwd_partial over
+ * disjoint key ranges of the same queries) into the attention over the union
+ * of the ranges: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s,
+ * rounded to bf16; rows that no part saw get O = 0, LSE = -inf.
+ *   O_parts: n_parts consecutive float32 [B,H,Sq,d] arrays; LSE_parts:
+ *   n_parts consecutive float32 [B,H,Sq] arrays (device memory, caller-owned,
+ *   read only).  O: bf16 [B,H,Sq,d] out; LSE: float32 [B,H,Sq] out.
+ *   n_parts >= 1; d in {64, 128}.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+fa_status fa_merge(const float* O_parts, const float* LSE_parts, int n_parts, int B, int H, int Sq, int d,
+                   void* O, float* LSE, void* stream);
+
 /* The share of exponentials fa_fwd computes in software for a requested
  * emu_frac (a pure function of its arguments; no HIP call). Negative when
  * the arguments are invalid. */

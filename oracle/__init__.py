@@ -25,6 +25,9 @@ Modules
   exp2_emulation   Cody-Waite range-reduced polynomial 2^x (paper §3.1.3,
                    Table 2) with the oracle's own minimax fit, bf16 rounding
                    and ULP distance.
+  partial          attention over one key range (output normalised over the
+                   range + its log-sum-exp) and the merge of such parts over
+                   disjoint ranges -- the single-GPU pieces of ring attention.
   roofline         per-tile cycle model (paper §3.1.1 Table 1; §3.2.1 Eq. 7-8)
                    with B200 constants and with CDNA4 constants.
 
@@ -39,11 +42,12 @@ from .attention import attention_forward, attention_backward, attention_probs
 from .online_softmax import conditional_rescale_forward
 from .exp2_emulation import (fit_exp2_minimax, exp2_emulated_f32, bf16_round,
                              bf16_ulp_distance, relative_error_curve)
+from .partial import attention_partial, merge_partials
 from . import roofline
 
 __all__ = [
     "attention_forward", "attention_backward", "attention_probs",
     "conditional_rescale_forward",
     "fit_exp2_minimax", "exp2_emulated_f32", "bf16_round", "bf16_ulp_distance",
-    "relative_error_curve", "roofline",
+    "relative_error_curve", "attention_partial", "merge_partials", "roofline",
 ]

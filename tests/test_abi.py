@@ -60,6 +60,36 @@ def test_fwd_rejects_before_any_launch(L, kw, status):
     assert _fwd(L, **kw) == status
 
 
+def test_partial_and_merge_validation(L):
+    vp = ctypes.c_void_p
+
+    def part(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=32, d=64, q_off=0, kb=0, ke=32,
+                 causal=0, scale=0.125, tau=8.0, emu=0.0)
+        a.update(kw)
+        return L.fa_fwd_partial(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["lse"]), a["B"], a["H"],
+                                a["Sq"], a["Sk"], a["d"], a["q_off"], a["kb"], a["ke"], a["causal"], a["scale"],
+                                a["tau"], a["emu"], vp(0))
+    assert part(kb=5, ke=5) == fa.FA_ERR_INVALID        # empty range
+    assert part(kb=-1) == fa.FA_ERR_INVALID
+    assert part(ke=33) == fa.FA_ERR_INVALID             # past Sk
+    assert part(q_off=-3) == fa.FA_ERR_INVALID
+    assert part(o=0) == fa.FA_ERR_INVALID
+    assert part(causal=2) == fa.FA_ERR_INVALID
+    assert part(d=80) == fa.FA_ERR_UNSUPPORTED
+
+    def merge(**kw):
+        a = dict(op=FAKE, lp=FAKE, n=2, B=1, H=1, Sq=16, d=64, o=FAKE, lse=FAKE)
+        a.update(kw)
+        return L.fa_merge(vp(a["op"]), vp(a["lp"]), a["n"], a["B"], a["H"], a["Sq"], a["d"], vp(a["o"]),
+                          vp(a["lse"]), vp(0))
+    assert merge(n=0) == fa.FA_ERR_INVALID
+    assert merge(op=0) == fa.FA_ERR_INVALID
+    assert merge(o=FAKE + 4) == fa.FA_ERR_INVALID
+    assert merge(Sq=0) == fa.FA_ERR_INVALID
+    assert merge(d=96) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_bwd_validation_and_workspace(L):
     vp = ctypes.c_void_p
     ws = fa.fa_bwd_workspace_bytes(1, 2, 100, 100, 64, True, True)
