@@ -70,14 +70,20 @@ def time_calls(fn, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
-def kernel_sources_sha256():
-    """Hash of the HIP sources the kernels are built from (ties a counter
-    summary in profiles/ to the kernel version it measured)."""
+# the source file of each kernel; every kernel also depends on the shared headers
+KERNEL_SOURCE = {"fwd_kernel": "fa_fwd.hip", "bwd_prep_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip",
+                 "bwd_dkdv_kernel": "fa_bwd.hip", "merge_kernel": "fa_merge.hip"}
+
+
+def kernel_sources_sha256(kernel):
+    """Hash of the HIP sources `kernel` is built from: its own .hip file and
+    the shared headers (ties a counter summary in profiles/ to the kernel
+    version it measured)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_50_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
+        if f.endswith((".hpp", ".h")) or f == KERNEL_SOURCE[kernel]:
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
@@ -95,7 +101,7 @@ def read_traffic(kernel, workload):
         if ":" in line and line.strip().startswith("- "):
             key, val = line.strip()[2:].split(":", 1)
             fields[key.strip()] = val.strip().strip("`")
-    if fields.get("source_sha256") != kernel_sources_sha256():
+    if fields.get("source_sha256") != kernel_sources_sha256(kernel):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))

@@ -98,6 +98,18 @@ __device__ __forceinline__ float exp2_sw(float x) {
   return x < -126.0f ? 0.0f : r;
 }
 
+// x if C <= lim, else -inf: one compare into VCC and one select, so that a
+// run of these keeps no lane masks alive in scalar registers.
+template <int C>
+__device__ __forceinline__ float keep_if_le(float x, int lim) {
+  float r;
+  asm("v_cmp_le_i32 vcc, %2, %3\n\tv_cndmask_b32 %0, %4, %1, vcc"
+      : "=v"(r)
+      : "v"(x), "i"(C), "v"(lim), "v"(kNegInf)
+      : "vcc");
+  return r;
+}
+
 // Exchange a value with the other half of the wave (lane l <-> l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 

@@ -49,8 +49,11 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;               // query rows per wavefront
 constexpr int kBM = kWaves * kQW;     // query rows per workgroup
-constexpr int kBN = 64;               // keys per tile
-constexpr int kStages = 4;
+// keys per tile: 128 in the 256-row form (two 2-stage rings, K and V), 64 in
+// the split form (one 4-stage ring of K+V stages)
+constexpr int kBNFull = 128;
+constexpr int kBNSplit = 64;
+constexpr int kStages = 4;            // split form
 
 struct FwdParams {
   const bf16* q;
@@ -69,12 +72,21 @@ struct FwdParams {
   float tau;
 };
 
-template <int D>
+// LDS of the 256-row form: K ring of 2 stages, then V ring of 2 stages, each
+// stage one 128-key tile.  Split form: 4 stages of (K tile, V tile) of 64
+// keys.  Both take 4 * 128 * 2D bytes (128 KiB at D = 128).
+template <int D, bool SPLIT>
 struct FwdLayout {
+  static constexpr int kBN = SPLIT ? kBNSplit : kBNFull;
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileBytes = kBN * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kLdsBytes = SPLIT ? kStages * 2 * kTileBytes : 4 * kTileBytes;
+  __device__ __forceinline__ static char* k_stage(char* smem, int u) {
+    return SPLIT ? smem + (u & (kStages - 1)) * 2 * kTileBytes : smem + (u & 1) * kTileBytes;
+  }
+  __device__ __forceinline__ static char* v_stage(char* smem, int u) {
+    return SPLIT ? smem + (u & (kStages - 1)) * 2 * kTileBytes + kTileBytes : smem + (2 + (u & 1)) * kTileBytes;
+  }
 };
 
 constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
@@ -87,7 +99,8 @@ constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
 // leave the chip waiting on the heaviest.
 template <int D, bool CAUSAL, int EMU, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
-  using L = FwdLayout<D>;
+  using L = FwdLayout<D, SPLIT>;
+  constexpr int kBN = L::kBN;
   constexpr int kKB = kBN / 32;   // 32-key blocks per tile
   constexpr int kKS = kBN / 16;   // 16-key steps of P V
   constexpr int kDB = D / 32;     // 32-dim blocks of the output
@@ -184,8 +197,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     constexpr bool SK = decltype(with_s)::value;
     constexpr int j0 = PV ? 0 : kNV;
     constexpr int j1 = SK ? kNV + kNK : kNV;
-    const char* vst = smem + (uv & (kStages - 1)) * L::kStageBytes + L::kTileBytes;
-    const char* kst = smem + (uk & (kStages - 1)) * L::kStageBytes;
+    const char* vst = L::v_stage(smem, uv);
+    const char* kst = L::k_stage(smem, uk);
     // j < kNV: (ks, db) = (j / kDB, j % kDB); j >= kNV: (kc, kb) = (i / kKB, i % kKB), i = j - kNV
     auto operand = [&](int j) __attribute__((always_inline)) -> bf16x8 {
       if (j < kNV) return read_cols<D>(vst, v_lane, j / kDB, j % kDB);
@@ -237,13 +250,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int k0 = tile_of(t) * kBN;
     const bool need_mask = (k0 + kBN > p.k_len) || (CAUSAL && k0 + kBN - 1 > q_diag + q_wave_lo);
     if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= p.k_len || (CAUSAL && key > q_diag + q_lane)) s[kb][i] = kNegInf;
-        }
+      // the keys a row sees form a prefix of the tile: score (kb, i) of this
+      // lane is key k0 + 32 kb + 8 (i / 4) + 4 g + i % 4, kept iff that key
+      // is below k_len (and, causal, at most the row's diagonal)
+      const int last = CAUSAL ? min(p.k_len - 1, q_diag + q_lane) : p.k_len - 1;
+      const int lim = last - k0 - 4 * g;
+      static_for<kKB * 16>([&](auto e) __attribute__((always_inline)) {
+        constexpr int kb = decltype(e)::value / 16, i = decltype(e)::value % 16;
+        s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
+      });
     }
     // row max: 8 independent chains, then a short tree
     float m8[8];
@@ -274,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float x = __builtin_fmaf(s[kb][i], p.scale_log2, neg_m);
-        const float e = (kb * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
+        const float e = ((kb & 1) * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
         s[kb][i] = e;
         l_part[i & 3] += e;
       }
@@ -286,12 +301,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // Tile IO.  The 256-row form loads each K/V tile straight into its LDS
-  // stage (memory-to-LDS loads, no registers): tile u is issued where
-  // fetch(u) stands, in interval 2u-3, once its stage's previous tile (u-4)
-  // has been read for the last time, and commit(u), at the end of interval
-  // 2u-2, only waits for the tile before it (u-1, first read in interval
-  // 2u-1), so every tile has about three intervals to arrive.  The split
+  // Tile IO.  The 256-row form loads tiles straight into LDS (memory-to-LDS
+  // loads, no registers).  Tile u's K is read in intervals 2u+1 and 2u+2 (the
+  // S products of the two groups) and its V in 2u+3 and 2u+4 (their P V
+  // products).  With two stages per ring, K_u replaces K_{u-2} (last read in
+  // interval 2u-2) and V_u replaces V_{u-2} (last read in 2u), so interval
+  // 2u-1 issues K_u and V_{u-1} (fetch(u)) and the end of interval 2u waits
+  // for them (commit): every load has two intervals to arrive.  The split
   // form writes tile k+1's stage in the interval right after tile k-3's last
   // read; it stages tiles through registers (fetch one interval ahead, write
   // to LDS at the start of the next), so the global load gets a whole
@@ -299,25 +315,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // past the last tile that costs a little bandwidth (rows past the head
   // read as zeros) and saves the register copies a conditional load needs.
   TileIO<D, kBN, kWaves> kio, vio;
-  constexpr int kDmaPerTile = 2 * TileDMA<D, kBN, kWaves>::kLoads;   // per wave
+  using DMA = TileDMA<D, kBN, kWaves>;
   auto fetch = [&](int u) __attribute__((always_inline)) {
     if constexpr (SPLIT) {
       kio.fetch(rk, u * kBN, wave, lane);
       vio.fetch(rv, u * kBN, wave, lane);
-    } else if (u < n) {
-      char* st = smem + (u & (kStages - 1)) * L::kStageBytes;
-      TileDMA<D, kBN, kWaves>::load(rk, u * kBN, st, wave, lane);
-      TileDMA<D, kBN, kWaves>::load(rv, u * kBN, st + L::kTileBytes, wave, lane);
+    } else {
+      if (u < n) DMA::load(rk, u * kBN, L::k_stage(smem, u), wave, lane);
+      if (u >= 1 && u <= n) DMA::load(rv, (u - 1) * kBN, L::v_stage(smem, u - 1), wave, lane);
     }
   };
   auto commit = [&](int u) __attribute__((always_inline)) {
     if constexpr (SPLIT) {
-      char* st = smem + (u & (kStages - 1)) * L::kStageBytes;
-      kio.store(st, wave, lane);
-      vio.store(st + L::kTileBytes, wave, lane);
-    } else if (u < n) {
-      // tile u's loads are the newest; everything older is complete
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerTile) : "memory");
+      kio.store(L::k_stage(smem, u), wave, lane);
+      vio.store(L::v_stage(smem, u), wave, lane);
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -380,43 +391,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     //   group 1: interval 1 idle; 2t+2 matrix(t), 2t+3 vector(t); 2n+2 matrix(n)
     // matrix(t) = O += V_{t-1} P_{t-1} (t > 0) and S_t = K_t Q^T (t < n_wave);
     // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
-    // n_wave - 1 but keeps taking part in the barriers.  Every wave issues
-    // its loads of tile u into stage u % 4 in interval 2u-3 (fetch) and
-    // waits for those of tile u-1 at the end of interval 2u-2 (commit);
-    // tile u is read in intervals 2u+1 .. 2u+4.  Each variant of the matrix
-    // phase appears in a straight-line position of its own so the
-    // accumulators are never merged across branches.  Prologue: after
-    // commit(1) (which waits for tile 0) and the barrier, tile 0 is readable.
+    // n_wave - 1 but keeps taking part in the barriers and the loads.  Every
+    // wave issues its share of fetch(u) in interval 2u-1 and commits at the
+    // end of every even interval.  Each variant of the matrix phase appears
+    // in a straight-line position of its own so the accumulators are never
+    // merged across branches.  Prologue: K_0 is loaded and readable in
+    // interval 1.
     fetch(0);
     commit(0);
-    fetch(1);
-    commit(1);
     barrier();
     if (group == 0) {
-      fetch(2);
+      fetch(1);
       matrix_s(0);
       barrier();
       vector(0);
-      commit(2);
+      commit(0);
       barrier();
       for (int t = 1; t < n_wave; ++t) {
-        fetch(t + 2);
+        fetch(t + 1);
         matrix_full(t);
         barrier();
         vector(t);
-        commit(t + 2);
+        commit(0);
         barrier();
       }
       if (n_wave < n) {
-        fetch(n_wave + 2);
+        fetch(n_wave + 1);
         matrix_pv(n_wave);
         barrier();
-        commit(n_wave + 2);
+        commit(0);
         barrier();
         for (int t = n_wave + 1; t < n; ++t) {
-          fetch(t + 2);
+          fetch(t + 1);
           barrier();
-          commit(t + 2);
+          commit(0);
           barrier();
         }
         barrier();
@@ -427,32 +435,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         barrier();
       }
     } else {
-      fetch(2);
+      fetch(1);
       barrier();
       matrix_s(0);
-      commit(2);
+      commit(0);
       barrier();
-      fetch(3);
+      fetch(2);
       vector(0);
       barrier();
       for (int t = 1; t < n_wave; ++t) {
         matrix_full(t);
-        commit(t + 2);
+        commit(0);
         barrier();
-        fetch(t + 3);
+        fetch(t + 2);
         vector(t);
         barrier();
       }
       if (n_wave < n) {
         matrix_pv(n_wave);
-        commit(n_wave + 2);
+        commit(0);
         barrier();
-        fetch(n_wave + 3);
+        fetch(n_wave + 2);
         barrier();
         for (int t = n_wave + 1; t < n; ++t) {
-          commit(t + 2);
+          commit(0);
           barrier();
-          fetch(t + 3);
+          fetch(t + 2);
           barrier();
         }
         barrier();
@@ -462,7 +470,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       }
     }
   }
-
   float l_lane = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   if constexpr (SPLIT) {
     // group 1 hands (O, row sum, reference max) of each lane to the lane of
@@ -532,13 +539,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   }
 }
 
-// Software-exponential counts per lane per tile that are instantiated.
+// Software-exponential counts per 32 scores of a lane (64 keys) that are
+// instantiated.
 constexpr int kEmuCounts[] = {0, 3, 8, 16, 32};
 
 template <int D, bool CAUSAL, int EMU, bool SPLIT>
 hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
   auto kern = fwd_kernel<D, CAUSAL, EMU, SPLIT>;
-  const int lds = FwdLayout<D>::kLdsBytes;
+  const int lds = FwdLayout<D, SPLIT>::kLdsBytes;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
@@ -566,7 +574,8 @@ constexpr int kSplitBelowBlocks = 512;
 
 }  // namespace
 
-int fwd_exps_per_lane_tile(int /*d*/) { return kBN / 32 * 16; }
+// the software share is placed per 64 keys (32 scores of a lane) in both forms
+int fwd_exps_per_lane_tile(int /*d*/) { return 32; }
 
 int fwd_nearest_emu_count(int d, float emu_frac) {
   const float want = emu_frac * (float)fwd_exps_per_lane_tile(d);

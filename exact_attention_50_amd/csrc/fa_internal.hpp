@@ -23,7 +23,8 @@ struct FwdArgs {
   int emu_count;  // exponentials per lane per tile computed in software
 };
 
-// Per-lane exponentials of one forward tile (BN keys x 32 queries / 64 lanes).
+// Exponentials of one lane per 64 keys (64 keys x 32 queries / 64 lanes): the
+// unit over which the software share is placed.
 int fwd_exps_per_lane_tile(int d);
 // Software-exponential counts the forward kernel is instantiated for.
 int fwd_nearest_emu_count(int d, float emu_frac);

@@ -44,14 +44,16 @@ def test_small_shapes_every_element(d, Sq, Sk, causal):
     check_forward(o, lse, O, L, f"d{d} {Sq}x{Sk} c{causal}")
 
 
-def test_causal_full_blocks_every_element():
-    """Causal with enough heads for 256-row workgroups (small shapes and the
-    16-head workloads run the split 128-row form)."""
-    say("fwd causal B1 H128 S1000 d128 (256-row workgroups)")
-    q, k, v = make_inputs(1, 128, 1000, 1000, 128, seed=21)
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_full_blocks_every_element(d):
+    """Causal with enough heads for 256-row workgroups and 128-key tiles
+    (small shapes and the 16-head workloads run the split 128-row form);
+    S = 1000 leaves a ragged last tile and block."""
+    say(f"fwd causal B1 H128 S1000 d{d} (256-row workgroups)")
+    q, k, v = make_inputs(1, 128, 1000, 1000, d, seed=21 + d)
     o, lse = run_fwd(q, k, v, True)
-    O, L = attention_forward(q, k, v, 1 / math.sqrt(128), True)
-    say(check_forward(o, lse, O, L, "causal H128 S1000"))
+    O, L = attention_forward(q, k, v, 1 / math.sqrt(d), True)
+    say(check_forward(o, lse, O, L, f"causal H128 S1000 d{d}"))
 
 
 def test_config1_tiny_full():
