@@ -17,7 +17,11 @@ FLOP/clk), a roofline entry for the dominant kernel, the CPU oracle timed on
 a bounded sample of the same workload, and per-kernel / per-workload
 details (including the long causal forward, B=1 H=16 S=8192 d=128).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Before the W warmup steps the step runs untimed for --warm-seconds (default
+1 s) so that the GPU clocks have reached their sustained level; each forward
+sweep workload is warmed the same way for a third of that.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds T]
 """
 import argparse
 import json
@@ -37,8 +41,11 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warm-seconds", type=float, default=1.0,
+                   help="untimed run of the step before the warmup steps, so the GPU clocks "
+                        "reach their sustained level (each forward sweep workload gets a third)")
     p.add_argument("--workload", type=int, default=5, help="workload id in workloads.WORKLOADS")
     p.add_argument("--tau", type=float, default=8.0)
     p.add_argument("--emu", type=float, default=0.0)
@@ -54,9 +61,22 @@ def parse():
     return p.parse_args()
 
 
-def time_calls(fn, n, warmup):
+def warm_gpu(fn, seconds):
+    """Call fn() repeatedly for about `seconds` of wall time (untimed).  Under
+    sustained load the MI355X shader clock settles within a fraction of a
+    second; timing a cold GPU reads up to ~15 % slow."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_calls(fn, n, warmup, warm_s=0.0):
     """Mean milliseconds of fn() over n calls, HIP events on the current stream."""
     import torch
+    warm_gpu(fn, warm_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -202,7 +222,13 @@ def main():
                   ("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_DQ)),
                   ("bwd_dkdv_kernel", lambda: bwd_phase(fa.FA_BWD_DKDV))]
 
-    # ---- warmup, then exactly K timed steps with events between kernels
+    # ---- clock warm-up and W warmup steps, then exactly K timed steps with
+    # events between kernels
+    def step():
+        for _, fn in parts:
+            fn()
+
+    warm_gpu(step, args.warm_seconds)
     for _ in range(args.warmup):
         for _, fn in parts:
             fn()
@@ -255,7 +281,8 @@ def main():
             ll = torch.empty(qq.shape[:3], dtype=torch.float32, device=dev)
             for emu in ww.emu_fracs:
                 ms = time_calls(lambda: fa.fa_fwd(qq, kk, vv, oo, ll, causal=ww.causal, scale=ww.scale,
-                                                  tau=args.tau, emu_frac=emu), max(10, args.steps), 3)
+                                                  tau=args.tau, emu_frac=emu), max(10, args.steps), 3,
+                                args.warm_seconds / 3)
                 tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
                 extra[f"{ww.name}" + (f"-emu{emu:g}" if len(ww.emu_fracs) > 1 else "")] = {
                     "ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
@@ -278,8 +305,8 @@ def main():
                 fa.fa_fwd_partial(qq, kk, vv, op[i], lp[i], 0, bounds[i], bounds[i + 1], causal=True,
                                   scale=ww.scale, tau=args.tau)
 
-        ms_p = time_calls(partials, max(10, args.steps), 3)
-        ms_m = time_calls(lambda: fa.fa_merge(op, lp, om, lm), max(10, args.steps), 3)
+        ms_p = time_calls(partials, max(10, args.steps), 3, args.warm_seconds / 3)
+        ms_m = time_calls(lambda: fa.fa_merge(op, lp, om, lm), max(10, args.steps), 3, args.warm_seconds / 3)
         rows = ww.B * ww.H * ww.Sq
         merge_bytes = n_parts * rows * (ww.d * 4 + 4) + rows * (ww.d * 2 + 4)
         gbs = merge_bytes / (ms_m * 1e-3) / 1e9
@@ -302,6 +329,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_seconds": args.warm_seconds,
         "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
