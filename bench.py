@@ -287,6 +287,16 @@ def main():
                 extra[f"{ww.name}" + (f"-emu{emu:g}" if len(ww.emu_fracs) > 1 else "")] = {
                     "ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                     "emu_realised": round(fa.fa_fwd_realised_emu_frac(ww.d, emu), 4)}
+            if wid == 4:
+                # ablation of the conditional rescale: tau = 0 corrects the
+                # output on every increase of a row max (the eager online softmax)
+                ms = time_calls(lambda: fa.fa_fwd(qq, kk, vv, oo, ll, causal=ww.causal, scale=ww.scale,
+                                                  tau=0.0, emu_frac=0.0), max(10, args.steps), 3,
+                                args.warm_seconds / 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}-emu0-tau0"] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                    "emu_realised": 0.0, "tau": 0.0}
             del del_ins, qq, kk, vv, oo, ll
 
         # split-KV: the causal S=8192 workload as 4 key ranges (fa_fwd_partial

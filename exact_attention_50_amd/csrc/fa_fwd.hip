@@ -514,20 +514,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const float l = pair_sum(l_lane);
   const bool empty = !(l > 0.0f);
   const float inv_l = empty ? 0.0f : 1.0f / l;
-  if (!SPLIT && !p.o32) {
-    // bf16 output of the 256-row form, stored as whole rows.  In the MFMA
-    // layout a lane holds 8-byte pieces of one row, so a direct store would
-    // touch 32 rows per instruction; instead each wave stages its 32 x D
-    // output rows in a private LDS area (idle after the last barrier: every
-    // tile read and load has completed) and stores 16 bytes per lane, one
-    // instruction covering 64 x 16 consecutive bytes of consecutive rows.  The
-    // row pitch is padded by 16 bytes, so the 8-byte writes of a wave meet
-    // every bank once per 16 rows.
+  if (!p.o32) {
+    // bf16 output, stored as whole rows.  In the MFMA layout a lane holds
+    // 8-byte pieces of one row, so a direct store would touch 32 rows per
+    // instruction; instead each wave stages its 32 x D output rows in a
+    // private LDS area and stores 16 bytes per lane, one instruction covering
+    // 64 x 16 consecutive bytes of consecutive rows.  The areas lie in the
+    // ring, idle after the last barrier (every tile read and load has
+    // completed); in the split form they follow the merge area, which the
+    // other waves of group 0 may still be reading.  The row pitch is padded
+    // by 16 bytes, so the 8-byte writes of a wave meet every bank once per
+    // 16 rows.
     constexpr int kPitch = D * 2 + 16;
     constexpr int kChunks = D / 8;   // 16-byte chunks per row
     constexpr int kRowsPerStore = 64 / kChunks;
-    static_assert(kWaves * kQW * kPitch <= L::kLdsBytes, "output staging exceeds the LDS ring");
-    char* stage = smem + wave * (kQW * kPitch);
+    constexpr int kStageBase = SPLIT ? kDB * 4 * 256 * 16 + 2 * 256 * 4 : 0;
+    constexpr int kStagingWaves = SPLIT ? kWaves / 2 : kWaves;
+    static_assert(kStageBase + kStagingWaves * kQW * kPitch <= L::kLdsBytes, "output staging exceeds the LDS ring");
+    char* stage = smem + kStageBase + (SPLIT ? (wave & 3) : wave) * (kQW * kPitch);
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -548,26 +552,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     if (q_lane < p.Sq && g == 0)
       p.lse[(size_t)bh * p.Sq + q_lane] = empty ? kNegInf : (m_ref + __builtin_log2f(l)) * kLn2;
   } else if (q_lane < p.Sq) {
-    if (p.o32) {
-      float* orow = p.o32 + ((size_t)bh * p.Sq + q_lane) * D;
+    // float32 output (key-range parts): 16-byte pieces, stored directly
+    float* orow = p.o32 + ((size_t)bh * p.Sq + q_lane) * D;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) =
-              f32x4{o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
-                    o[db][4 * i4 + 3] * inv_l};
-    } else {
-      bf16* orow = p.o + ((size_t)bh * p.Sq + q_lane) * D;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 v4 = {o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
-                            o[db][4 * i4 + 3] * inv_l};
-          *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
-        }
-    }
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i4 + 4 * g) =
+            f32x4{o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
+                  o[db][4 * i4 + 3] * inv_l};
     if (g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = empty ? kNegInf : (m_ref + __builtin_log2f(l)) * kLn2;
   }
 }
