@@ -341,17 +341,11 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   // ---- dQ = scale (dQ^T)^T -> bf16 (lane = query, 4 consecutive dims per group)
 #pragma unroll
   for (int db = 0; db < kDB; ++db) mfma_drain_a(dq[db]);
-  if (q_ok) {
-    bf16* row = p.dq + ((size_t)bh * p.Sq + qi) * D;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = {dq[db][4 * i4] * p.scale, dq[db][4 * i4 + 1] * p.scale, dq[db][4 * i4 + 2] * p.scale,
-                          dq[db][4 * i4 + 3] * p.scale};
-        *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
-      }
-  }
+  // whole-row stores through LDS, once every wave has read its last tile
+  static_assert(kWaves * RowStore<D>::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+  dma_barrier();
+  RowStore<D>::store(smem + wave * RowStore<D>::kBytes, dq, p.scale, p.dq + (size_t)bh * p.Sq * D,
+                     q0 + wave * kQW, p.Sq, lane);
 }
 
 // =================================================================== dK dV
@@ -642,21 +636,13 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
     mfma_drain_a(dk[db]);
     mfma_drain_a(dv[db]);
   }
-  if (key < p.Sk) {
-    bf16* dkr = p.dk + ((size_t)bh * p.Sk + key) * D;
-    bf16* dvr = p.dv + ((size_t)bh * p.Sk + key) * D;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int c = db * 32 + 8 * i4 + 4 * g;
-        const f32x4 a = {dk[db][4 * i4] * p.scale, dk[db][4 * i4 + 1] * p.scale, dk[db][4 * i4 + 2] * p.scale,
-                         dk[db][4 * i4 + 3] * p.scale};
-        const f32x4 b = {dv[db][4 * i4], dv[db][4 * i4 + 1], dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]};
-        *reinterpret_cast<bf16x4*>(dkr + c) = __builtin_convertvector(a, bf16x4);
-        *reinterpret_cast<bf16x4*>(dvr + c) = __builtin_convertvector(b, bf16x4);
-      }
-  }
+  // whole-row stores through LDS, once every wave has read its last tile
+  using RS = RowStore<D>;
+  static_assert(2 * kWaves * RS::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+  dma_barrier();
+  RS::store(smem + wave * RS::kBytes, dk, p.scale, p.dk + (size_t)bh * p.Sk * D, k0 + wave * kKW, p.Sk, lane);
+  RS::store(smem + (kWaves + wave) * RS::kBytes, dv, 1.0f, p.dv + (size_t)bh * p.Sk * D, k0 + wave * kKW, p.Sk,
+            lane);
 }
 
 template <typename K>

@@ -515,40 +515,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const bool empty = !(l > 0.0f);
   const float inv_l = empty ? 0.0f : 1.0f / l;
   if (!p.o32) {
-    // bf16 output, stored as whole rows.  In the MFMA layout a lane holds
-    // 8-byte pieces of one row, so a direct store would touch 32 rows per
-    // instruction; instead each wave stages its 32 x D output rows in a
-    // private LDS area and stores 16 bytes per lane, one instruction covering
-    // 64 x 16 consecutive bytes of consecutive rows.  The areas lie in the
+    // bf16 output, stored as whole rows through a per-wave LDS area in the
     // ring, idle after the last barrier (every tile read and load has
-    // completed); in the split form they follow the merge area, which the
-    // other waves of group 0 may still be reading.  The row pitch is padded
-    // by 16 bytes, so the 8-byte writes of a wave meet every bank once per
-    // 16 rows.
-    constexpr int kPitch = D * 2 + 16;
-    constexpr int kChunks = D / 8;   // 16-byte chunks per row
-    constexpr int kRowsPerStore = 64 / kChunks;
+    // completed); in the split form the areas follow the merge area, which
+    // the other waves of group 0 may still be reading
+    using RS = RowStore<D>;
     constexpr int kStageBase = SPLIT ? kDB * 4 * 256 * 16 + 2 * 256 * 4 : 0;
     constexpr int kStagingWaves = SPLIT ? kWaves / 2 : kWaves;
-    static_assert(kStageBase + kStagingWaves * kQW * kPitch <= L::kLdsBytes, "output staging exceeds the LDS ring");
-    char* stage = smem + kStageBase + (SPLIT ? (wave & 3) : wave) * (kQW * kPitch);
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v4 = {o[db][4 * i4 + 0] * inv_l, o[db][4 * i4 + 1] * inv_l, o[db][4 * i4 + 2] * inv_l,
-                          o[db][4 * i4 + 3] * inv_l};
-        *reinterpret_cast<bf16x4*>(stage + r32 * kPitch + (db * 32 + 8 * i4 + 4 * g) * 2) =
-            __builtin_convertvector(v4, bf16x4);
-      }
-    const int c = lane % kChunks;
-#pragma unroll
-    for (int j = 0; j < kQW / kRowsPerStore; ++j) {
-      const int row = j * kRowsPerStore + lane / kChunks;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * kPitch + c * 16);
-      if (q_wave_lo + row < p.Sq)
-        *reinterpret_cast<u32x4*>(p.o + ((size_t)bh * p.Sq + q_wave_lo + row) * D + c * 8) = val;
-    }
+    static_assert(kStageBase + kStagingWaves * RS::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+    RS::store(smem + kStageBase + (SPLIT ? (wave & 3) : wave) * RS::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * D,
+              q_wave_lo, p.Sq, lane);
     if (q_lane < p.Sq && g == 0)
       p.lse[(size_t)bh * p.Sq + q_lane] = empty ? kNegInf : (m_ref + __builtin_log2f(l)) * kLn2;
   } else if (q_lane < p.Sq) {

@@ -130,4 +130,41 @@ struct TileDMA {
   }
 };
 
+// Output of a wave's 32 x D accumulator block as bf16 rows.  In the MFMA C
+// layout of X^T a lane holds 8-byte pieces of one row of X (acc[db][i] is
+// X[r][32 db + 8 (i / 4) + 4 g + i % 4] for lane r + 32 g), so storing from
+// registers touches 32 rows per instruction.  The block, times mul (per lane,
+// i.e. per row), is staged in `stage` (kBytes of LDS private to the wave, rows
+// padded by 16 bytes so the 8-byte writes meet every bank once per 16 rows)
+// and stored 16 bytes per lane over consecutive rows: rows row0 .. row0 + 31
+// of out (row pitch D elements), skipping rows >= n_rows.
+template <int D>
+struct RowStore {
+  static constexpr int kPitch = D * 2 + 16;
+  static constexpr int kBytes = 32 * kPitch;
+
+  __device__ __forceinline__ static void store(char* stage, const f32x16* acc, float mul, bf16* out, int row0,
+                                               int n_rows, int lane) {
+    const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v = {acc[db][4 * i4 + 0] * mul, acc[db][4 * i4 + 1] * mul, acc[db][4 * i4 + 2] * mul,
+                         acc[db][4 * i4 + 3] * mul};
+        *reinterpret_cast<bf16x4*>(stage + r * kPitch + (db * 32 + 8 * i4 + 4 * g) * 2) =
+            __builtin_convertvector(v, bf16x4);
+      }
+    constexpr int kChunks = D / 8;   // 16-byte chunks per row
+    constexpr int kRowsPerStore = 64 / kChunks;
+    const int c = lane % kChunks;
+#pragma unroll
+    for (int j = 0; j < 32 / kRowsPerStore; ++j) {
+      const int row = j * kRowsPerStore + lane / kChunks;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * kPitch + c * 16);
+      if (row0 + row < n_rows) *reinterpret_cast<u32x4*>(out + (size_t)(row0 + row) * D + c * 8) = val;
+    }
+  }
+};
+
 }  // namespace fa
