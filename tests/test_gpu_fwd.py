@@ -44,16 +44,17 @@ def test_small_shapes_every_element(d, Sq, Sk, causal):
     check_forward(o, lse, O, L, f"d{d} {Sq}x{Sk} c{causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_causal_full_blocks_every_element(d):
-    """Causal with enough heads for 256-row workgroups and 128-key tiles
-    (small shapes and the 16-head workloads run the split 128-row form);
-    S = 1000 leaves a ragged last tile and block."""
-    say(f"fwd causal B1 H128 S1000 d{d} (256-row workgroups)")
-    q, k, v = make_inputs(1, 128, 1000, 1000, d, seed=21 + d)
-    o, lse = run_fwd(q, k, v, True)
-    O, L = attention_forward(q, k, v, 1 / math.sqrt(d), True)
-    say(check_forward(o, lse, O, L, f"causal H128 S1000 d{d}"))
+@pytest.mark.parametrize("d,S,causal", [(64, 1000, True), (128, 1000, True), (64, 1200, True), (64, 1000, False)])
+def test_full_blocks_every_element(d, S, causal):
+    """Enough heads for 256-row workgroups with 128-key tiles (small shapes
+    and the 16-head causal workloads run the split 128-row form instead).
+    S = 1000 leaves a ragged last tile and block; S = 1200 an odd number of
+    query blocks."""
+    say(f"fwd B1 H128 S{S} d{d} causal={causal} (256-row workgroups)")
+    q, k, v = make_inputs(1, 128, S, S, d, seed=21 + d + S)
+    o, lse = run_fwd(q, k, v, causal)
+    O, L = attention_forward(q, k, v, 1 / math.sqrt(d), causal)
+    say(check_forward(o, lse, O, L, f"H128 S{S} d{d} causal={causal}"))
 
 
 def test_config1_tiny_full():
