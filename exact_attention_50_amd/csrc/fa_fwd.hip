@@ -30,11 +30,13 @@
 //   * O^T = V^T P^T: the S^T accumulator, rounded to bf16, is already the B
 //     operand (keys of each 16-key group in a fixed permuted order); the V^T
 //     A operand is read from row-major V in LDS with ds_read_b64_tr_b16;
-//   * K / V tiles: 4-stage LDS ring with the chunk permutation of
-//     fa_tiles.hpp (bank-conflict-free operand reads), loaded memory-to-LDS
-//     about three phases ahead of their first read (the split form stages
-//     them through registers instead); buffer descriptors bound every head,
-//     so rows past the end read zeros.
+//   * K / V tiles with the chunk permutation of fa_tiles.hpp (bank-conflict-
+//     free operand reads): the 256-row form streams 128-key tiles through a
+//     2-stage K ring and a 2-stage V ring, loaded memory-to-LDS two intervals
+//     ahead of their first read; the split form streams 64-key tiles through
+//     a 4-stage K+V ring, staged through registers; buffer descriptors bound
+//     every head, so rows past the end read zeros;
+//   * the bf16 output leaves through a per-wave LDS area as whole rows.
 
 #include <type_traits>
 
