@@ -273,8 +273,9 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for wid in (2, 3, 4):
-            ww = WORKLOADS[wid]
+        from workloads import EXTRA_WORKLOADS
+        for wid in (2, 3, 4, 6):
+            ww = WORKLOADS[wid] if wid in WORKLOADS else EXTRA_WORKLOADS[wid]
             del_ins = [t.to(dev) for t in workload_inputs(ww)]
             qq, kk, vv = del_ins[:3]
             oo = torch.empty_like(qq)

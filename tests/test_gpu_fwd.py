@@ -90,6 +90,16 @@ def test_config2_sampled():
     say(st)
 
 
+def test_extra_noncausal_long_sampled():
+    """The supplementary non-causal S = 8192, d = 128 forward the benchmark
+    reports (labelled extra), on sampled heads and rows."""
+    from workloads import EXTRA_WORKLOADS
+    w = EXTRA_WORKLOADS[6]
+    say(f"fwd {w.name}")
+    st = _sampled(w, [(0, 0), (0, 11)], _rows(w.Sq, 32, 6))
+    say(st)
+
+
 def test_config3_causal_long_sampled():
     w = WORKLOADS[3]
     say(f"fwd {w.name}")

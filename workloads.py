@@ -58,6 +58,12 @@ WORKLOADS = {
     5: Workload("bwd-causal-B1H16S4096d128", 1, 16, 4096, 4096, 128, True, seed=5, kind="bwd"),
 }
 
+# Supplementary shapes, reported beside the configurations above and labelled
+# as extra: the non-causal forward at S = 8192, d = 128.
+EXTRA_WORKLOADS = {
+    6: Workload("extra-fwd-noncausal-B1H16S8192d128", 1, 16, 8192, 8192, 128, False, seed=6),
+}
+
 
 def make_inputs(B, H, Sq, Sk, d, seed, key_ramp=0.0, with_dout=False, heads=None):
     """Draw bf16 Q, K, V (and dO) on the CPU.
