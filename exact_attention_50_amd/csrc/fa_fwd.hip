@@ -262,16 +262,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
       });
     }
-    // row max: 8 independent chains, then a short tree
+    // row max: 8 independent chains of v_max3_f32 (two scores per
+    // instruction), then a short tree
+    constexpr int kPerChain = kKB * 16 / 8;
+    auto score = [&](int e) __attribute__((always_inline)) -> float { return s[e / 16][e % 16]; };
     float m8[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) m8[c] = s[0][c];
+    for (int c = 0; c < 8; ++c) {
+      m8[c] = score(c);
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int i = (kb == 0 ? 8 : 0); i < 16; ++i) m8[i & 7] = __builtin_fmaxf(m8[i & 7], s[kb][i]);
-    float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
-                               __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
+      for (int k = 1; k + 1 < kPerChain; k += 2) m8[c] = max3(m8[c], score(c + 8 * k), score(c + 8 * (k + 1)));
+      // (max3 with a repeated operand, so no fmaxf has to canonicalise an asm result)
+      if constexpr (kPerChain % 2 == 0) {
+        const float x = score(c + 8 * (kPerChain - 1));
+        m8[c] = max3(m8[c], x, x);
+      }
+    }
+    float mx = max3(max3(m8[0], m8[1], m8[2]), max3(m8[3], m8[4], m8[5]), max3(m8[6], m8[7], m8[7]));
     mx = pair_max(mx);
     const float m_new = __builtin_fmaxf(m_ref, mx * p.scale_log2);
     // conditional rescale: wave-uniform branch; only rows whose max rose by
