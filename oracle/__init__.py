@@ -28,6 +28,8 @@ Modules
   partial          attention over one key range (output normalised over the
                    range + its log-sum-exp) and the merge of such parts over
                    disjoint ranges -- the single-GPU pieces of ring attention.
+  fp8              e4m3 decoding, exact attention of dequantised e4m3 inputs,
+                   and the per-element error bound of rounding P to e4m3.
   roofline         per-tile cycle model (paper §3.1.1 Table 1; §3.2.1 Eq. 7-8)
                    with B200 constants and with CDNA4 constants.
 
@@ -43,6 +45,7 @@ from .online_softmax import conditional_rescale_forward
 from .exp2_emulation import (fit_exp2_minimax, exp2_emulated_f32, bf16_round,
                              bf16_ulp_distance, relative_error_curve)
 from .partial import attention_partial, merge_partials
+from .fp8 import e4m3_decode, attention_fp8_reference, fp8_output_bound
 from . import roofline
 
 __all__ = [
@@ -50,4 +53,5 @@ __all__ = [
     "conditional_rescale_forward",
     "fit_exp2_minimax", "exp2_emulated_f32", "bf16_round", "bf16_ulp_distance",
     "relative_error_curve", "attention_partial", "merge_partials", "roofline",
+    "e4m3_decode", "attention_fp8_reference", "fp8_output_bound",
 ]

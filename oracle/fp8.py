@@ -1,0 +1,72 @@
+"""Attention on e4m3 (FP8) inputs, in float64 -- test infrastructure only.
+
+What it computes.  The FA4 paper summary ("FlashAttention-4: Algorithm and
+Kernel Pipelining Co-Design for Asymmetric Hardware Scaling", precision
+discussion) names FP8 as the next operand format.  Inputs are e4m3 codes
+with one dequantisation factor per tensor, so the attention they stand for is
+the ordinary exact attention of the dequantised tensors:
+
+  Q = q_descale * e4m3(Q8),  K = k_descale * e4m3(K8),  V = v_descale * e4m3(V8),
+  O, LSE = attention_forward(Q, K, V)   (the definition in ``attention``).
+
+e4m3 here is the OCP 8-bit format with 4 exponent bits (bias 7), 3 mantissa
+bits, subnormals, no infinities and one NaN pattern per sign (S.1111.111);
+the largest finite value is 448.  ``e4m3_decode`` writes that definition out.
+
+Rounding the probabilities.  A kernel that rounds its unnormalised
+probabilities P_j = 2^(s_j - m) (m at most the row's max, so the largest
+P_j >= 1) to e4m3 before P V, while normalising by the sum l of the unrounded
+P_j, is off from the exact O by at most
+
+  sum_j (2^-4 P_j + 2^-10 [P_j < 2^-6]) |v_j| / l
+      <= 2^-4 sum_j p_j |v_j| + 2^-10 sum_j |v_j| / l_max
+
+per output element (round-to-nearest: half an e4m3 step is 2^-4 of the value
+for normal values and 2^-10 below 2^-6; p = exact softmax weights; l_max =
+sum_j exp(s_j - max_j s_j) <= l).  ``fp8_output_bound`` returns that bound
+per element; the LSE is unaffected (the row sum uses the unrounded P).
+
+Pins (tests/test_oracle_fp8.py): the decoder against the format's named
+values (0, min subnormal 2^-9, min normal 2^-6, 1, 448, NaN) and against
+torch's float8_e4m3fn on all 256 codes; the bound holds for a brute-force
+attention that rounds P with torch's e4m3 conversion.
+"""
+import numpy as np
+
+from .attention import _f64, attention_forward, attention_probs
+
+
+def e4m3_decode(codes):
+    """float64 values of e4m3 codes (uint8 array or tensor)."""
+    c = np.asarray(codes.cpu().numpy() if hasattr(codes, "cpu") else codes).astype(np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def dequantise(codes, descale):
+    return e4m3_decode(codes) * float(descale)
+
+
+def attention_fp8_reference(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
+    """(O, LSE) of exact attention on the dequantised e4m3 inputs."""
+    return attention_forward(dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale),
+                             scale, causal)
+
+
+def fp8_output_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
+    """Per-element bound [B,H,Sq,d] on |O_kernel - O_exact| from rounding the
+    unnormalised probabilities to e4m3 (see the module text)."""
+    q, k, v = dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale)
+    p = attention_probs(q, k, scale, causal)                 # exact softmax weights
+    av = np.abs(_f64(v))
+    rel = np.einsum("bhij,bhjc->bhic", p, av)                # sum_j p_j |v_j|
+    # l_max = 1 / max_j p_j (the row sum relative to the row's max score)
+    lmax = 1.0 / np.max(p, axis=-1, keepdims=True)
+    Sq, Sk = p.shape[-2], p.shape[-1]
+    vis = np.tril(np.ones((Sq, Sk))) if causal else np.ones((Sq, Sk))   # visible keys
+    absum = np.einsum("ij,bhjc->bhic", vis, av)                          # sum_j |v_j| over them
+    return 2.0 ** -4 * rel + 2.0 ** -10 * absum / lmax

@@ -91,3 +91,13 @@ def make_inputs(B, H, Sq, Sk, d, seed, key_ramp=0.0, with_dout=False, heads=None
 def workload_inputs(w, heads=None):
     return make_inputs(w.B, w.H, w.Sq, w.Sk, w.d, w.seed, key_ramp=w.key_ramp,
                        with_dout=(w.kind == "bwd"), heads=heads)
+
+
+def quantise_e4m3(x, amax=224.0):
+    """e4m3 codes (uint8, torch's round-to-nearest float8_e4m3fn conversion)
+    and the per-tensor dequantisation factor of a float tensor: x is divided
+    by max|x| / amax first, so its largest magnitude lands on amax (half of
+    e4m3's 448, leaving room for rounding)."""
+    descale = float(x.abs().max()) / amax if float(x.abs().max()) > 0 else 1.0
+    codes = (x.float() / descale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, descale
