@@ -45,6 +45,8 @@ def lib():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, f, vp]
+    L.fa_fwd_fp8.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd_partial.restype = i
     L.fa_merge.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
@@ -116,6 +118,35 @@ def fa_fwd(q, k, v, o, lse, causal=False, scale=None, tau=8.0, emu_frac=0.0):
                       float(scale), float(tau), float(emu_frac), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
+
+
+def _check_e4m3(name, t, shape):
+    import torch
+    if (t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_cuda or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name}: expected a contiguous e4m3 (float8_e4m3fn or uint8) CUDA tensor of shape "
+                         f"{tuple(shape)}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0):
+    """Enqueue the e4m3 forward on the current stream; fills the bf16 o and
+    the float32 lse in place.  q8, k8, v8 hold e4m3 bytes (float8_e4m3fn or
+    uint8); the attention is computed on q_descale * q8, k_descale * k8,
+    v_descale * v8."""
+    B, H, Sq, d = q8.shape
+    Sk = k8.shape[2]
+    _check_e4m3("q8", q8, (B, H, Sq, d))
+    _check_e4m3("k8", k8, (B, H, Sk, d))
+    _check_e4m3("v8", v8, (B, H, Sk, d))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale), float(v_descale),
+                          _ptr(o), _ptr(lse), B, H, Sq, Sk, d, int(bool(causal)), float(scale), float(tau),
+                          _stream(q8))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
 
 
 def fa_fwd_partial(q, k, v, o_part, lse_part, q_offset, k_begin, k_end, causal=False, scale=None, tau=8.0,
@@ -201,6 +232,16 @@ def fa_exp2_probe(x, y_hw, y_emu):
 
 
 # ------------------------------------------------------ allocating helpers
+def forward_fp8(q8, k8, v8, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0):
+    """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq]) of the e4m3 forward."""
+    import torch
+    B, H, Sq, d = q8.shape
+    o = torch.empty((B, H, Sq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, v8, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, tau=tau)
+    return o, lse
+
+
 def forward(q, k, v, causal=False, scale=None, tau=8.0, emu_frac=0.0):
     """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq])."""
     import torch

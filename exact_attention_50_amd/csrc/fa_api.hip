@@ -71,6 +71,32 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_descale, float k_descale,
+                     float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal, float scale,
+                     float tau, void* stream) {
+  if (!Q8 || !K8 || !V8 || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(Q8) || !aligned16(K8) || !aligned16(V8) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  for (float f : {q_descale, k_descale, v_descale})
+    if (!(isfinite(f) && f > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdFp8Args a;
+  a.q = Q8; a.k = K8; a.v = V8; a.o = O; a.lse = LSE;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
+  a.tau = tau;
+  const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_partial(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part, int B, int H,
                          int Sq, int Sk, int d, int q_offset, int k_begin, int k_end, int causal, float scale,
                          float tau, float emu_frac, void* stream) {

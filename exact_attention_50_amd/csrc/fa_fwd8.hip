@@ -1,0 +1,432 @@
+// Fused exact-attention forward with e4m3 (FP8) operands, for gfx950.
+//
+// The method is that of the bf16 forward (FlashAttention-4 paper as
+// summarised on "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design
+// for Asymmetric Hardware Scaling", Method: online softmax over key tiles,
+// conditional rescaling of the running output while the row max grows by at
+// most tau, one division by the row sum at the end); the summary's precision
+// discussion names FP8 as the next operand format.  Here Q, K and V arrive as
+// e4m3 bytes with one dequantisation factor per tensor:
+//   S = (scale * q_descale * k_descale) * Q8 K8^T        (fp32 accumulation)
+//   P = 2^(S log2(e) - m_ref), rounded to e4m3 (P <= 2^tau <= 256 < 448)
+//   O = v_descale * (P8 V8) / l,  l = sum of the fp32 P (before rounding)
+//   LSE from the fp32 scores and l, as in the bf16 forward.
+//
+// CDNA4 mapping (ours): the 256-row workgroup, the two wave groups alternating
+// matrix and softmax phases, and the 2-stage K and V rings of 128-key tiles of
+// the bf16 forward, with
+//   * products v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3, scales 1): A and
+//     B lanes hold 32 consecutive k (lane l: row l % 32, k 32 (l / 32) .. +31);
+//     the C layout is the bf16 32x32 one, so the softmax code is unchanged;
+//   * e4m3 tiles of 128 keys x 128 bytes; the 16-byte chunk c of row r sits at
+//     chunk position c ^ ((r >> 1) & 7), so 16 consecutive rows read at one
+//     chunk meet 16 distinct 16-byte bank slots;
+//   * S^T = K Q^T: K is the A operand (two 16-byte reads of one row), Q^T the
+//     B operand in registers;
+//   * O^T += V^T P^T per 64 keys: P^T (B operand) is two S^T accumulators
+//     rounded to e4m3, so lane (r, g) holds the keys
+//     32 (j / 16) + 8 ((j % 16) / 4) + 4 g + j % 4 at k-slot 32 g + j; the V^T A
+//     operand follows that order through ds_read_b64_tr_b8, which gives lane i
+//     of a 16-lane group byte i % 8 of the 8-byte chunks addressed by lanes
+//     2 m + i / 8 (m = 0..7): the even lanes address dims 0-7 and the odd
+//     lanes dims 8-15 of the same 8 keys, four reads give the 32 k-slots.
+
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+#include "fa_tiles.hpp"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves8 = 8;
+constexpr int kThreads8 = kWaves8 * 64;
+constexpr int kQW8 = 32;                 // query rows per wave
+constexpr int kBM8 = kWaves8 * kQW8;     // query rows per workgroup
+constexpr int kBN8 = 128;                // keys per tile
+constexpr int kD8 = 128;                 // head dimension = bytes per row
+constexpr int kTile8 = kBN8 * kD8;       // 16 KiB
+constexpr int kRing8 = 4 * kTile8;       // K stages 0, 1 then V stages 0, 1
+constexpr int kLds8 = kRing8 > kWaves8 * RowStore<kD8>::kBytes ? kRing8 : kWaves8 * RowStore<kD8>::kBytes;
+constexpr int kAhead8 = 2;               // operands in flight per wave (64-cycle products)
+
+struct Fwd8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  bf16* o;
+  float* lse;
+  int BH, Sq, Sk, n_qblocks;
+  float s_log2;      // scale * q_descale * k_descale * log2(e)
+  float v_descale;
+  float tau;
+};
+
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// byte offset of chunk c (16 bytes) of row r in a tile
+__device__ __forceinline__ int off8(int r, int c) { return r * kD8 + 16 * (c ^ swz8(r)); }
+
+// e4m3 x e4m3 products written out as single instructions (the compiler
+// moves its own form of this product past barriers to the first use of the
+// result, which keeps every operand of a phase live at once).  The code
+// around them owns two latencies: the s_nop 1 in front covers a VALU write of
+// an operand just before, and drain8() (24 wait states, tied to the
+// accumulators) separates the last product of a phase from VALU reads.
+__device__ __forceinline__ void mfma8_acc(f32x16& d, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void mfma8_init(f32x16& d, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void drain8(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+
+// k-slot j of lane group g (0, 1) -> key of the 64-key step
+__device__ __forceinline__ int slot_key(int g, int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * g + (j % 4); }
+
+// a tile of 128 rows, memory-to-LDS with the chunk permutation: one 16-byte
+// load per lane covers 8 whole rows; a wave issues 2 of the 16
+__device__ __forceinline__ void dma_tile8(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kBN8 / 8 / kWaves8; ++i) {
+    const int blk = i * kWaves8 + wave;   // wave-uniform
+    const int row = blk * 8 + lane / 8;
+    const unsigned off = (unsigned)(row0 + row) * kD8 + 16 * ((lane % 8) ^ swz8(row));
+    lds_dma16(src, off, tile + blk * 8 * kD8);
+  }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
+  constexpr int kKB = kBN8 / 32;   // 32-key blocks of S^T per tile
+  constexpr int kKC = kD8 / 64;    // 64-dim steps of S^T
+  constexpr int kKS = kBN8 / 64;   // 64-key steps of P V
+  constexpr int kDB = kD8 / 32;    // 32-dim blocks of O^T
+  constexpr int kNV = kKS * kDB;   // P V products per tile
+  constexpr int kNK = kKB * kKC;   // K Q^T products per tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int rank = blockIdx.x / p.BH;
+  const int bh = blockIdx.x % p.BH;
+  const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * kD8, (unsigned)p.Sq * kD8);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
+
+  const int q_wave_lo = qb * kBM8 + wave * kQW8;
+  const int q_lane = q_wave_lo + r32;
+
+  // Q^T operand, k-step kc: lane holds Q[q_lane][64 kc + 32 g .. +31]
+  i32x8 qf[kKC];
+#pragma unroll
+  for (int kc = 0; kc < kKC; ++kc) {
+    qf[kc].lo = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g));
+    qf[kc].hi = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g + 16));
+  }
+
+  // K operand addresses: row 32 kb + r32 has the chunk permutation of r32
+  const int k_sw = swz8(r32);
+  const int k_row = r32 * kD8;
+  // V^T operand addresses: read q of a 64-key step; this lane, as a source
+  // lane of its 16-lane group, addresses the key of k-slot 8 q + m (m = (lane
+  // % 16) / 2) and the dims 32 db + 16 half + 8 par .. +7 (half = group of
+  // 16 lanes within the wave half, par = lane parity)
+  const int par = lane & 1;
+  const int m8 = (lane & 15) >> 1;
+  const int half = (lane >> 4) & 1;
+  // offset of read q, dims 32 db + ..: row slot_key(g, 8 q + m8) (the key of
+  // step ks adds 64 rows, which keeps the permutation), chunk 2 db + half,
+  // i.e. v_base[q] + ((32 db) ^ v_x[q]) with the chunk permutation split
+  // into its half and db bits
+  int v_base[4], v_x[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = slot_key(g, 8 * q + m8);
+    const int sw = swz8(row);
+    v_base[q] = row * kD8 + 8 * par + 16 * (half ^ (sw & 1));
+    v_x[q] = 32 * (sw >> 1);
+  }
+
+  const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM8) : p.Sk;
+  const int n = (kv_end + kBN8 - 1) / kBN8;
+  int n_wave = CAUSAL ? max(1, min(n, (q_wave_lo + kQW8 + kBN8 - 1) / kBN8)) : n;
+  if (CAUSAL) asm volatile("" : "+s"(n_wave));
+
+  f32x16 o[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
+  f32x16 s[kKB];
+  i32x8 pk[kKS];
+  float m_ref = kNegInf;
+  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto k_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (u & 1) * kTile8; };
+  auto v_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (2 + (u & 1)) * kTile8; };
+
+  // ---- matrix phase: O^T += V^T P^T of tile uv, then S^T = K Q^T of tile uk
+  auto matrix_stream_body = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value;
+    constexpr bool SK = decltype(with_s)::value;
+    constexpr int j0 = PV ? 0 : kNV;
+    constexpr int j1 = SK ? kNV + kNK : kNV;
+    const char* vst = v_stage(uv);
+    const char* kst = k_stage(uk);
+    // the 16 read offsets are formed per read (one xor-add each) rather than
+    // kept live across the loop, which would not fit the register budget
+    int vb[4], vx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      vb[q] = v_base[q];
+      vx[q] = v_x[q];
+      asm volatile("" : "+v"(vb[q]), "+v"(vx[q]));
+    }
+    // j < kNV: (ks, db) = (j / kDB, j % kDB); else (kb, kc) = (i % kKB, i / kKB), i = j - kNV
+    auto operand = [&](int j) __attribute__((always_inline)) -> i32x8 {
+      if (j < kNV) {
+        const int ks = j / kDB, db = j % kDB;
+        i32x8 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const char* a = vst + ks * 64 * kD8 + vb[q] + ((32 * db) ^ vx[q]);
+          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2*)(lds_addr(a)));
+          r[2 * q] = t[0];
+          r[2 * q + 1] = t[1];
+        }
+        return r;
+      }
+      const int i = j - kNV;
+      const int kb = i % kKB, kc = i / kKB;
+      const char* row = kst + kb * 32 * kD8 + k_row;
+      i32x8 r;
+      r.lo = *reinterpret_cast<const i32x4*>(row + 16 * ((4 * kc + 2 * g) ^ k_sw));
+      r.hi = *reinterpret_cast<const i32x4*>(row + 16 * ((4 * kc + 2 * g + 1) ^ k_sw));
+      return r;
+    };
+    i32x8 ring[kAhead8];
+#pragma unroll
+    for (int j = j0; j < j0 + kAhead8 && j < j1; ++j) ring[(j - j0) % kAhead8] = operand(j);
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const i32x8 a = ring[(j - j0) % kAhead8];
+      if (j + kAhead8 < j1) ring[(j - j0) % kAhead8] = operand(j + kAhead8);
+      if (j < kNV) {
+        mfma8_acc(o[j % kDB], a, pk[j / kDB]);
+      } else {
+        const int i = j - kNV;   // the first k-step starts each accumulator
+        if (i < kKB)
+          mfma8_init(s[i % kKB], a, qf[i / kKB]);
+        else
+          mfma8_acc(s[i % kKB], a, qf[i / kKB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (PV) drain8(o[0], o[1], o[2], o[3]);
+    if (SK) drain8(s[0], s[1], s[2], s[3]);
+  };
+  auto matrix_stream = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    matrix_stream_body(uk, uv, with_pv, with_s);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto matrix_s = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(t, 0, std::false_type{}, std::true_type{});
+  };
+  auto matrix_full = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(t, t - 1, std::true_type{}, std::true_type{});
+  };
+  auto matrix_pv = [&](int t) __attribute__((always_inline)) {
+    matrix_stream(0, t - 1, std::true_type{}, std::false_type{});
+  };
+
+  // ---- vector phase: softmax of tile t, P rounded to e4m3
+  auto vector = [&](int t) __attribute__((always_inline)) {
+    if (t >= n_wave) return;
+    const int k0 = t * kBN8;
+    const bool need_mask = (k0 + kBN8 > p.Sk) || (CAUSAL && k0 + kBN8 - 1 > q_wave_lo);
+    if (need_mask) {
+      const int last = CAUSAL ? min(p.Sk - 1, q_lane) : p.Sk - 1;
+      const int lim = last - k0 - 4 * g;
+      static_for<kKB * 16>([&](auto e) __attribute__((always_inline)) {
+        constexpr int kb = decltype(e)::value / 16, i = decltype(e)::value % 16;
+        s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
+      });
+    }
+    constexpr int kPerChain = kKB * 16 / 8;
+    auto score = [&](int e) __attribute__((always_inline)) -> float { return s[e / 16][e % 16]; };
+    float m8c[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      m8c[c] = score(c);
+#pragma unroll
+      for (int k = 1; k + 1 < kPerChain; k += 2) m8c[c] = max3(m8c[c], score(c + 8 * k), score(c + 8 * (k + 1)));
+      if constexpr (kPerChain % 2 == 0) {
+        const float x = score(c + 8 * (kPerChain - 1));
+        m8c[c] = max3(m8c[c], x, x);
+      }
+    }
+    float mx = max3(max3(m8c[0], m8c[1], m8c[2]), max3(m8c[3], m8c[4], m8c[5]), max3(m8c[6], m8c[7], m8c[7]));
+    mx = pair_max(mx);
+    const float m_new = __builtin_fmaxf(m_ref, mx * p.s_log2);
+    const bool need = (m_new - m_ref) > p.tau;
+    if (__any(need)) {
+      const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+      m_ref = need ? m_new : m_ref;
+    }
+    const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = exp2_hw(__builtin_fmaf(s[kb][i], p.s_log2, neg_m));
+        s[kb][i] = e;
+        l_part[i & 3] += e;
+      }
+    // P^T operand of 64-key step ks: bytes j = 0..31 are s[2 ks + j / 16][j % 16]
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * ks + w / 4, i0 = 4 * (w % 4);
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0 + 2], s[kb][i0 + 3], d, true);
+        pk[ks][w] = d;
+      }
+  };
+
+  // ---- tile IO: interval 2u-1 issues K_u and V_{u-1}; the end of every even
+  // interval waits for them (the schedule of the bf16 256-row form)
+  auto fetch = [&](int u) __attribute__((always_inline)) {
+    if (u < n) dma_tile8(rk, u * kBN8, k_stage(u), wave, lane);
+    if (u >= 1 && u <= n) dma_tile8(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
+  };
+  auto commit = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  fetch(0);
+  commit();
+  barrier();
+  if (group == 0) {
+    fetch(1);
+    matrix_s(0);
+    barrier();
+    vector(0);
+    commit();
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      fetch(t + 1);
+      matrix_full(t);
+      barrier();
+      vector(t);
+      commit();
+      barrier();
+    }
+    // the last P V (tile n_wave - 1) has one call site, so the accumulators
+    // are never merged across branches (the products are asm the compiler
+    // cannot see the latency of: a merge copy right after one would read a
+    // result not yet written); with n_wave = n, fetch(n + 1) loads nothing
+    fetch(n_wave + 1);
+    matrix_pv(n_wave);
+    barrier();
+    if (n_wave < n) {
+      commit();
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        fetch(t + 1);
+        barrier();
+        commit();
+        barrier();
+      }
+      barrier();
+    }
+    barrier();
+  } else {
+    fetch(1);
+    barrier();
+    matrix_s(0);
+    commit();
+    barrier();
+    fetch(2);
+    vector(0);
+    barrier();
+    for (int t = 1; t < n_wave; ++t) {
+      matrix_full(t);
+      commit();
+      barrier();
+      fetch(t + 2);
+      vector(t);
+      barrier();
+    }
+    matrix_pv(n_wave);
+    commit();
+    barrier();
+    if (n_wave < n) {
+      fetch(n_wave + 2);
+      barrier();
+      for (int t = n_wave + 1; t < n; ++t) {
+        commit();
+        barrier();
+        fetch(t + 2);
+        barrier();
+      }
+      barrier();
+    }
+  }
+
+  // ---- epilogue: O = v_descale O / l as bf16 rows, LSE = (m_ref + log2 l) ln 2
+  const float l = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+  const float inv_l = l > 0.0f ? p.v_descale / l : 0.0f;
+  RowStore<kD8>::store(smem + wave * RowStore<kD8>::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * kD8, q_wave_lo,
+                       p.Sq, lane);
+  if (q_lane < p.Sq && g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = (m_ref + __builtin_log2f(l)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
+  Fwd8Params prm;
+  prm.q = static_cast<const uint8_t*>(a.q);
+  prm.k = static_cast<const uint8_t*>(a.k);
+  prm.v = static_cast<const uint8_t*>(a.v);
+  prm.o = static_cast<bf16*>(a.o);
+  prm.lse = a.lse;
+  prm.BH = a.B * a.H;
+  prm.Sq = a.Sq;
+  prm.Sk = a.Sk;
+  prm.n_qblocks = (a.Sq + kBM8 - 1) / kBM8;
+  prm.s_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
+  prm.v_descale = a.v_descale;
+  prm.tau = a.tau;
+  const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
+  auto run = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds8);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads8), kLds8, stream, prm);
+    return hipGetLastError();
+  };
+  return a.causal ? run(fwd8_kernel<true>) : run(fwd8_kernel<false>);
+}
+
+}  // namespace fa

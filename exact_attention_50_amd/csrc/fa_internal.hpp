@@ -31,6 +31,20 @@ int fwd_nearest_emu_count(int d, float emu_frac);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
+// e4m3 forward (d = 128): Q, K, V are e4m3 bytes dequantised by one factor
+// each; O bf16, LSE float32
+struct FwdFp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Sq, Sk;
+  bool causal;
+  float scale, q_descale, k_descale, v_descale, tau;
+};
+hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
+
 // rows = B * H * Sq; parts are n_parts consecutive [rows, d] / [rows] arrays
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int d, void* o,
                         float* lse, hipStream_t stream);

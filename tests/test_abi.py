@@ -27,7 +27,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_exp2_probe", "fa_status_str",
-            "fa_fwd_realised_emu_frac"} <= set(names)
+            "fa_fwd_realised_emu_frac", "fa_fwd_fp8"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -58,6 +58,23 @@ def _fwd(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=16, d=
 ])
 def test_fwd_rejects_before_any_launch(L, kw, status):
     assert _fwd(L, **kw) == status
+
+
+def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, B=1, H=1, Sq=16, Sk=16, d=128,
+          causal=0, scale=0.125, tau=8.0):
+    vp = ctypes.c_void_p
+    return L.fa_fwd_fp8(vp(q), vp(k), vp(v), qs, ks, vs, vp(o), vp(lse), B, H, Sq, Sk, d, causal, scale, tau,
+                        vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=0), fa.FA_ERR_INVALID), (dict(k=FAKE + 8), fa.FA_ERR_INVALID), (dict(H=0), fa.FA_ERR_INVALID),
+    (dict(qs=0.0), fa.FA_ERR_INVALID), (dict(vs=-1.0), fa.FA_ERR_INVALID), (dict(ks=float("inf")), fa.FA_ERR_INVALID),
+    (dict(tau=8.5), fa.FA_ERR_INVALID), (dict(scale=-1.0), fa.FA_ERR_INVALID), (dict(causal=3), fa.FA_ERR_INVALID),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=8), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_fp8_rejects_before_any_launch(L, kw, status):
+    assert _fwd8(L, **kw) == status
 
 
 def test_partial_and_merge_validation(L):

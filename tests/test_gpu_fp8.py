@@ -1,0 +1,93 @@
+"""GPU parity of the e4m3 forward (fa_fwd_fp8) against the oracle: exact
+attention of the dequantised inputs, within the per-element bound of rounding
+the unnormalised probabilities to e4m3 (oracle.fp8_output_bound) plus the
+bf16 output rounding; LSE within the forward's LSE tolerance."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_50_amd as fa
+from oracle import attention_fp8_reference, e4m3_decode, fp8_output_bound
+from parity import LSE_REL, oracle_rows
+from workloads import make_inputs, quantise_e4m3
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SLACK = 2e-3   # float32 accumulation and exponentials, far below the bound
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def quantised(B, H, Sq, Sk, d, seed):
+    q, k, v = make_inputs(B, H, Sq, Sk, d, seed=seed)
+    (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.float()) for t in (q, k, v))
+    return q8, k8, v8, qs, ks, vs
+
+
+def run(q8, k8, v8, qs, ks, vs, causal, tau=8.0):
+    o, lse = fa.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, causal=causal, tau=tau)
+    torch.cuda.synchronize()
+    return o.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def check(o, lse, O, L, bound, what):
+    err = np.abs(o - O)
+    allowed = bound + 2.0 ** -8 * np.abs(O) + SLACK
+    lse_err = np.abs(lse - L) / np.maximum(1.0, np.abs(L))
+    stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), bound_max=float(bound.max()),
+                 worst_ratio=float((err / allowed).max()), lse_rel=float(lse_err.max()))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
+    assert np.all(err <= allowed), (what, stats)
+    assert stats["lse_rel"] <= LSE_REL, (what, stats)
+    return stats
+
+
+@pytest.mark.parametrize("Sq,Sk,causal", [(1, 1, False), (17, 17, True), (128, 128, False), (257, 257, True),
+                                          (200, 333, False), (384, 384, True)])
+def test_fp8_small_shapes_every_element(Sq, Sk, causal):
+    say(f"fp8 fwd B2 H3 Sq={Sq} Sk={Sk} causal={causal}")
+    d = 128
+    q8, k8, v8, qs, ks, vs = quantised(2, 3, Sq, Sk, d, seed=Sq * 7 + Sk)
+    o, lse = run(q8, k8, v8, qs, ks, vs, causal)
+    scale = 1 / math.sqrt(d)
+    O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, causal)
+    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+    say(check(o, lse, O, L, bound, f"{Sq}x{Sk} c{causal}"))
+
+
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_fp8_many_heads_every_element(tau):
+    """Enough heads for several rounds of workgroups, ragged length."""
+    say(f"fp8 fwd B1 H64 S1000 causal tau={tau}")
+    d = 128
+    q8, k8, v8, qs, ks, vs = quantised(1, 64, 1000, 1000, d, seed=31)
+    o, lse = run(q8, k8, v8, qs, ks, vs, True, tau=tau)
+    scale = 1 / math.sqrt(d)
+    O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
+    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, True)
+    say(check(o, lse, O, L, bound, f"H64 S1000 tau={tau}"))
+
+
+def test_fp8_long_causal_sampled():
+    """The causal B1 H16 S8192 d128 shape, sampled heads and rows (a causal
+    row is the non-causal result over its key prefix)."""
+    say("fp8 fwd B1 H16 S8192 causal, sampled")
+    B, H, S, d = 1, 16, 8192, 128
+    q8, k8, v8, qs, ks, vs = quantised(B, H, S, S, d, seed=3)
+    o, lse = run(q8, k8, v8, qs, ks, vs, True)
+    scale = 1 / math.sqrt(d)
+    rng = np.random.default_rng(3)
+    rows = sorted(set(rng.choice(S, size=24, replace=False).tolist()) | {0, 1, 255, 256, S - 1})
+    deq = [torch.from_numpy(e4m3_decode(t) * s) for t, s in ((q8, qs), (k8, ks), (v8, vs))]
+    for b, h in [(0, 0), (0, 9)]:
+        O, L = oracle_rows(deq[0], deq[1], deq[2], scale, True, [(b, h)], rows)
+        bound = np.stack([fp8_output_bound(q8[b:b + 1, h:h + 1, i:i + 1], k8[b:b + 1, h:h + 1, :i + 1],
+                                           v8[b:b + 1, h:h + 1, :i + 1], qs, ks, vs, scale, False)[0, 0, 0]
+                          for i in rows])
+        say(check(o[b, h, rows], lse[b, h, rows], O[0], L[0], bound, f"head {h}"))

@@ -160,3 +160,54 @@ def test_kernel_sources_found():
 def test_no_valu_write_right_before_mfma_read(src, kernel_assembly):
     bad = hazards(kernel_assembly[src])
     assert not bad, "VALU write then MFMA read without two wait states:\n" + "\n".join(bad[:20])
+
+
+def early_accumulator_reads(asm, mnemonic="v_mfma_f32_32x32x64_f8f6f4", drain_nops=3):
+    """For every `mnemonic` product written as inline asm, the instructions up
+    to the next drain (drain_nops consecutive `s_nop 7`, 24 wait states) that
+    read or write its accumulator other than further products.  The compiler
+    does not know these are MFMAs, so such an instruction -- typically a
+    register-allocation copy -- would read a result that is not yet written.
+    Straight-line scan per code path (labels end nothing: a product is always
+    drained in its own block in the kernels checked)."""
+    ins = [t for t, lab in instructions(asm) if not lab]
+    bad = []
+    for k, t in enumerate(ins):
+        if not t.startswith(mnemonic):
+            continue
+        dst = regs(t.split(",")[0])
+        nops = 0
+        for u in ins[k + 1:]:
+            if u.startswith("s_nop 7"):
+                nops += 1
+                if nops == drain_nops:
+                    break
+                continue
+            nops = 0
+            if u.startswith(mnemonic) or u.startswith("s_"):
+                continue
+            if regs(u) & dst:
+                bad.append(f"{t}  ->  {u}")
+                break
+    return bad
+
+
+@pytest.mark.parametrize("src", [s for s in KERNEL_SOURCES if os.path.basename(s) == "fa_fwd8.hip"],
+                         ids=os.path.basename)
+def test_fp8_products_drained_before_any_other_use(src, kernel_assembly):
+    asm = kernel_assembly[src]
+    assert asm.count("v_mfma_f32_32x32x64_f8f6f4") >= 16
+    bad = early_accumulator_reads(asm)
+    assert not bad, "accumulator used before the drain:\n" + "\n".join(bad[:20])
+
+
+def test_drain_scanner_finds_a_planted_copy():
+    planted = "\n".join([
+        "\tv_mfma_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], v[0:15]",
+        "\tv_mfma_f32_32x32x64_f8f6f4 v[32:47], v[16:23], v[24:31], v[32:47]",
+        "\tv_mov_b64_e32 v[50:51], v[14:15]",
+        "\ts_nop 7", "\ts_nop 7", "\ts_nop 7",
+        "\tv_mov_b64_e32 v[52:53], v[46:47]",
+    ])
+    bad = early_accumulator_reads(planted)
+    assert len(bad) == 1 and "v[50:51], v[14:15]" in bad[0], bad
