@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 
 
@@ -58,6 +59,8 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=0,
                    help="with --reps: first run --reps plain device copies of this many MiB "
                         "(a known byte count that scales the HBM counters)")
+    p.add_argument("--fp8", action="store_true",
+                   help="with --reps and --fwd-only: run the e4m3 forward on the quantised workload")
     return p.parse_args()
 
 
@@ -92,7 +95,7 @@ def time_calls(fn, n, warmup, warm_s=0.0):
 
 # the source file of each kernel; every kernel also depends on the shared headers
 KERNEL_SOURCE = {"fwd_kernel": "fa_fwd.hip", "bwd_prep_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip",
-                 "bwd_dkdv_kernel": "fa_bwd.hip", "merge_kernel": "fa_merge.hip"}
+                 "bwd_dkdv_kernel": "fa_bwd.hip", "merge_kernel": "fa_merge.hip", "fwd8_kernel": "fa_fwd8.hip"}
 
 
 def kernel_sources_sha256(kernel):
@@ -195,6 +198,15 @@ def main():
     if args.reps:
         # profiler mode: optional plain copies of known size (to scale HBM
         # counters), then K steps; prints one line and nothing else
+        if args.fp8:
+            if do_bwd:
+                sys.exit("--fp8 profiles the forward only: add --fwd-only")
+            from workloads import quantise_e4m3
+            (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.cpu()) for t in (q, k, v))
+            q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+
+            def fwd():
+                fa.fa_fwd_fp8(q8, k8, v8, o, lse, qs, ks, vs, causal=w.causal, scale=w.scale, tau=args.tau)
         if args.copy_mib:
             src = torch.ones(args.copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
@@ -207,7 +219,7 @@ def main():
             if do_bwd:
                 bwd()
         torch.cuda.synchronize()
-        print(f"ran {args.reps} steps of {w.name}" +
+        print(f"ran {args.reps} steps of {w.name}" + (" (e4m3 forward)" if args.fp8 else "") +
               (f" after {args.reps} copies of {args.copy_mib} MiB" if args.copy_mib else ""), flush=True)
         return
 
@@ -288,6 +300,20 @@ def main():
                 extra[f"{ww.name}" + (f"-emu{emu:g}" if len(ww.emu_fracs) > 1 else "")] = {
                     "ms": round(ms, 5), "tflops": round(tf, 2), "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                     "emu_realised": round(fa.fa_fwd_realised_emu_frac(ww.d, emu), 4)}
+            if wid in (3, 6):
+                # the same workload on e4m3 inputs (per-tensor descales), priced
+                # against the fp8 MFMA peak
+                from workloads import quantise_e4m3
+                (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.cpu()) for t in (qq, kk, vv))
+                q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+                ms = time_calls(lambda: fa.fa_fwd_fp8(q8, k8, v8, oo, ll, qs, ks, vs, causal=ww.causal,
+                                                      scale=ww.scale, tau=args.tau),
+                                max(10, args.steps), 3, args.warm_seconds / 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}-fp8"] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3",
+                    "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
+                del q8, k8, v8
             if wid == 4:
                 # ablation of the conditional rescale: tau = 0 corrects the
                 # output on every increase of a row max (the eager online softmax)
