@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
   f32x16 s[kKB];
   i32x8 pk[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) pk[ks] = i32x8{};
   float m_ref = kNegInf;
   float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -238,9 +240,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     if (SK) drain8(s[0], s[1], s[2], s[3]);
   };
   auto matrix_stream = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);
     matrix_stream_body(uk, uv, with_pv, with_s);
-    __builtin_amdgcn_s_setprio(0);
   };
   auto matrix_s = [&](int t) __attribute__((always_inline)) {
     matrix_stream(t, 0, std::false_type{}, std::true_type{});
@@ -255,6 +255,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   // ---- vector phase: softmax of tile t, P rounded to e4m3
   auto vector = [&](int t) __attribute__((always_inline)) {
     if (t >= n_wave) return;
+    // with e4m3 products the softmax's VALU work is the longer phase, so it
+    // (not the matrix phase, as in the bf16 kernel) gets the raised priority
+    __builtin_amdgcn_s_setprio(2);
     const int k0 = t * kBN8;
     const bool need_mask = (k0 + kBN8 > p.Sk) || (CAUSAL && k0 + kBN8 - 1 > q_wave_lo);
     if (need_mask) {
@@ -305,10 +308,13 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = 2 * ks + w / 4, i0 = 4 * (w % 4);
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], 0, false);
+        // the first conversion keeps the upper half of its destination, which
+        // the second one overwrites: pass the stale value rather than a zero
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0], s[kb][i0 + 1], pk[ks][w], false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i0 + 2], s[kb][i0 + 3], d, true);
         pk[ks][w] = d;
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- tile IO: interval 2u-1 issues K_u and V_{u-1}; the end of every even
