@@ -24,9 +24,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def quantised(B, H, Sq, Sk, d, seed):
-    q, k, v = make_inputs(B, H, Sq, Sk, d, seed=seed)
-    (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.float()) for t in (q, k, v))
+def quantised(B, H, Sq, Sk, d, seed, key_ramp=0.0, amax=224.0):
+    q, k, v = make_inputs(B, H, Sq, Sk, d, seed=seed, key_ramp=key_ramp)
+    (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.float(), amax) for t in (q, k, v))
     return q8, k8, v8, qs, ks, vs
 
 
@@ -72,6 +72,46 @@ def test_fp8_many_heads_every_element(tau):
     O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
     bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, True)
     say(check(o, lse, O, L, bound, f"H64 S1000 tau={tau}"))
+
+
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_fp8_key_ramp_every_element(tau):
+    """Keys biased along the queries' mean direction, growing over the key
+    index (six standard deviations of q.k by the last key): the row max rises
+    tile after tile, so the conditional rescale fires often (tau 0: at every
+    rise)."""
+    say(f"fp8 fwd B1 H4 S1536 causal key ramp tau={tau}")
+    d = 128
+    q8, k8, v8, qs, ks, vs = quantised(1, 4, 1536, 1536, d, seed=41, key_ramp=6.0)
+    o, lse = run(q8, k8, v8, qs, ks, vs, True, tau=tau)
+    scale = 1 / math.sqrt(d)
+    O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
+    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, True)
+    say(check(o, lse, O, L, bound, f"ramp tau={tau}"))
+
+
+def test_fp8_extreme_codes_and_zero_queries():
+    """Tensors scaled so their largest magnitudes land on e4m3's largest
+    finite value (448), and query rows of all-zero codes, whose attention is
+    the plain mean of the visible V rows."""
+    say("fp8 fwd B2 H2 S300 non-causal and causal, amax 448, zero query rows")
+    d = 128
+    q8, k8, v8, qs, ks, vs = quantised(2, 2, 300, 300, d, seed=43, amax=448.0)
+    assert int((q8 & 0x7F).max()) == 0x7E and int((v8 & 0x7F).max()) == 0x7E
+    q8[:, :, ::7] = 0
+    scale = 1 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = run(q8, k8, v8, qs, ks, vs, causal)
+        O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, causal)
+        bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+        say(check(o, lse, O, L, bound, f"amax 448 causal={causal}"))
+        # zero query rows: uniform weights, so O is the mean of the visible V rows
+        v = e4m3_decode(v8) * vs
+        for i in range(0, 300, 7):
+            n_vis = i + 1 if causal else 300
+            mean = v[:, :, :n_vis].mean(axis=2)
+            assert np.abs(O[:, :, i] - mean).max() < 1e-12
+            assert np.abs(L[:, :, i] - math.log(n_vis)).max() < 1e-12
 
 
 def test_fp8_long_causal_sampled():
