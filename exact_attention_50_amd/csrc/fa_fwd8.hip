@@ -149,16 +149,24 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   const int half = (lane >> 4) & 1;
   // offset of read q, dims 32 db + ..: row slot_key(g, 8 q + m8) (the key of
   // step ks adds 64 rows, which keeps the permutation), chunk 2 db + half,
-  // i.e. v_base[q] + ((32 db) ^ v_x[q]) with the chunk permutation split
-  // into its half and db bits
-  int v_base[4], v_x[4];
+  // with the chunk permutation split into its half and db bits; the 16
+  // offsets (and the 4 of the K reads) are formed once per lane, so a read
+  // costs one add of the stage base
+  int v_off[4][kDB];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = slot_key(g, 8 * q + m8);
     const int sw = swz8(row);
-    v_base[q] = row * kD8 + 8 * par + 16 * (half ^ (sw & 1));
-    v_x[q] = 32 * (sw >> 1);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+      v_off[q][db] = row * kD8 + 8 * par + 16 * (half ^ (sw & 1)) + ((32 * db) ^ (32 * (sw >> 1)));
   }
+  // K operand reads: 16-byte chunk 4 kc + 2 g + h of row r32, swizzled
+  int k_off[2][2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) k_off[kc][h] = k_row + 16 * ((4 * kc + 2 * g + h) ^ k_sw);
 
   const int kv_end = CAUSAL ? min(p.Sk, (qb + 1) * kBM8) : p.Sk;
   const int n = (kv_end + kBN8 - 1) / kBN8;
@@ -186,15 +194,6 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     constexpr int j1 = SK ? kNV + kNK : kNV;
     const char* vst = v_stage(uv);
     const char* kst = k_stage(uk);
-    // the 16 read offsets are formed per read (one xor-add each) rather than
-    // kept live across the loop, which would not fit the register budget
-    int vb[4], vx[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      vb[q] = v_base[q];
-      vx[q] = v_x[q];
-      asm volatile("" : "+v"(vb[q]), "+v"(vx[q]));
-    }
     // j < kNV: (ks, db) = (j / kDB, j % kDB); else (kb, kc) = (i % kKB, i / kKB), i = j - kNV
     auto operand = [&](int j) __attribute__((always_inline)) -> i32x8 {
       if (j < kNV) {
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
         i32x8 r;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const char* a = vst + ks * 64 * kD8 + vb[q] + ((32 * db) ^ vx[q]);
+          const char* a = vst + ks * 64 * kD8 + v_off[q][db];
           const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) i32x2*)(lds_addr(a)));
           r[2 * q] = t[0];
@@ -212,10 +211,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
       }
       const int i = j - kNV;
       const int kb = i % kKB, kc = i / kKB;
-      const char* row = kst + kb * 32 * kD8 + k_row;
+      const char* row = kst + kb * 32 * kD8;
       i32x8 r;
-      r.lo = *reinterpret_cast<const i32x4*>(row + 16 * ((4 * kc + 2 * g) ^ k_sw));
-      r.hi = *reinterpret_cast<const i32x4*>(row + 16 * ((4 * kc + 2 * g + 1) ^ k_sw));
+      r.lo = *reinterpret_cast<const i32x4*>(row + k_off[kc][0]);
+      r.hi = *reinterpret_cast<const i32x4*>(row + k_off[kc][1]);
       return r;
     };
     i32x8 ring[kAhead8];
