@@ -45,7 +45,7 @@ def lib():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd.restype = i
-    L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, f, vp]
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd_partial.restype = i
@@ -128,11 +128,13 @@ def _check_e4m3(name, t, shape):
                          f"{tuple(shape)}, got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0):
+def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0,
+               head_descales=None):
     """Enqueue the e4m3 forward on the current stream; fills the bf16 o and
     the float32 lse in place.  q8, k8, v8 hold e4m3 bytes (float8_e4m3fn or
     uint8); the attention is computed on q_descale * q8, k_descale * k8,
-    v_descale * v8."""
+    v_descale * v8, each factor times the (batch, head) slice's factor in
+    head_descales (None, or a float32 CUDA tensor [3, B, H]: Q, K, V)."""
     B, H, Sq, d = q8.shape
     Sk = k8.shape[2]
     _check_e4m3("q8", q8, (B, H, Sq, d))
@@ -140,9 +142,12 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, 
     _check_e4m3("v8", v8, (B, H, Sk, d))
     _check_bf16("o", o, (B, H, Sq, d))
     _check_f32("lse", lse, (B, H, Sq))
+    if head_descales is not None:
+        _check_f32("head_descales", head_descales, (3, B, H))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale), float(v_descale),
+                          None if head_descales is None else _ptr(head_descales),
                           _ptr(o), _ptr(lse), B, H, Sq, Sk, d, int(bool(causal)), float(scale), float(tau),
                           _stream(q8))
     if st != FA_OK:
@@ -232,13 +237,15 @@ def fa_exp2_probe(x, y_hw, y_emu):
 
 
 # ------------------------------------------------------ allocating helpers
-def forward_fp8(q8, k8, v8, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0):
+def forward_fp8(q8, k8, v8, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False, scale=None, tau=8.0,
+                head_descales=None):
     """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq]) of the e4m3 forward."""
     import torch
     B, H, Sq, d = q8.shape
     o = torch.empty((B, H, Sq, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
-    fa_fwd_fp8(q8, k8, v8, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, tau=tau)
+    fa_fwd_fp8(q8, k8, v8, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, tau=tau,
+               head_descales=head_descales)
     return o, lse
 
 

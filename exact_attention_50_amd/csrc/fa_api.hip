@@ -72,9 +72,10 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
 }
 
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_descale, float k_descale,
-                     float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal, float scale,
-                     float tau, void* stream) {
+                     float v_descale, const float* head_descales, void* O, float* LSE, int B, int H, int Sq, int Sk,
+                     int d, int causal, float scale, float tau, void* stream) {
   if (!Q8 || !K8 || !V8 || !O || !LSE) return FA_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(head_descales) % alignof(float) != 0) return FA_ERR_INVALID;
   if (!aligned16(Q8) || !aligned16(K8) || !aligned16(V8) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
   if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
   if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
@@ -92,6 +93,7 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
   a.causal = causal != 0;
   a.scale = scale;
   a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
+  a.head_descales = head_descales;
   a.tau = tau;
   const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -10,6 +10,8 @@
 //   S = (scale * q_descale * k_descale) * Q8 K8^T        (fp32 accumulation)
 //   P = 2^(S log2(e) - m_ref), rounded to e4m3 (P <= 2^tau <= 256 < 448)
 //   O = v_descale * (P8 V8) / l,  l = sum of the fp32 P (before rounding)
+// where each descale is the per-tensor factor times, optionally, a factor
+// of the (batch, head) slice.
 //   LSE from the fp32 scores and l, as in the bf16 forward.
 //
 // CDNA4 mapping (ours): the 256-row workgroup, the two wave groups alternating
@@ -62,6 +64,7 @@ struct Fwd8Params {
   int BH, Sq, Sk, n_qblocks;
   float s_log2;      // scale * q_descale * k_descale * log2(e)
   float v_descale;
+  const float* hd;   // null, or per-slice factors [3][BH] (q, k, v)
   float tau;
 };
 
@@ -121,6 +124,11 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 
   const int rank = blockIdx.x / p.BH;
   const int bh = blockIdx.x % p.BH;
+  float s_log2 = p.s_log2, v_descale = p.v_descale;
+  if (p.hd) {
+    s_log2 *= p.hd[bh] * p.hd[p.BH + bh];
+    v_descale *= p.hd[2 * p.BH + bh];
+  }
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * kD8, (unsigned)p.Sq * kD8);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     }
     float mx = max3(max3(m8c[0], m8c[1], m8c[2]), max3(m8c[3], m8c[4], m8c[5]), max3(m8c[6], m8c[7], m8c[7]));
     mx = pair_max(mx);
-    const float m_new = __builtin_fmaxf(m_ref, mx * p.s_log2);
+    const float m_new = __builtin_fmaxf(m_ref, mx * s_log2);
     const bool need = (m_new - m_ref) > p.tau;
     if (__any(need)) {
       const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = exp2_hw(__builtin_fmaf(s[kb][i], p.s_log2, neg_m));
+        const float e = exp2_hw(__builtin_fmaf(s[kb][i], s_log2, neg_m));
         s[kb][i] = e;
         l_part[i & 3] += e;
       }
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 
   // ---- epilogue: O = v_descale O / l as bf16 rows, LSE = (m_ref + log2 l) ln 2
   const float l = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-  const float inv_l = l > 0.0f ? p.v_descale / l : 0.0f;
+  const float inv_l = l > 0.0f ? v_descale / l : 0.0f;
   RowStore<kD8>::store(smem + wave * RowStore<kD8>::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * kD8, q_wave_lo,
                        p.Sq, lane);
   if (q_lane < p.Sq && g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = (m_ref + __builtin_log2f(l)) * kLn2;
@@ -422,6 +430,7 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
   prm.n_qblocks = (a.Sq + kBM8 - 1) / kBM8;
   prm.s_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
   prm.v_descale = a.v_descale;
+  prm.hd = a.head_descales;
   prm.tau = a.tau;
   const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
   auto run = [&](auto kern) -> hipError_t {

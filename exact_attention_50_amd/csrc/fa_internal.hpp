@@ -42,6 +42,7 @@ struct FwdFp8Args {
   int B, H, Sq, Sk;
   bool causal;
   float scale, q_descale, k_descale, v_descale, tau;
+  const float* head_descales;   // null or [3][B*H] on the device
 };
 hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
 

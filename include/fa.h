@@ -79,7 +79,11 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  * FlashAttention-4 summary's precision discussion.  Q8, K8, V8 are e4m3
  * bytes, [B,H,Sq,d], [B,H,Sk,d], [B,H,Sk,d]; the attention is computed on
  * Q = q_descale * Q8, K = k_descale * K8, V = v_descale * V8 (descales > 0,
- * finite).  Scores accumulate in float32; the unnormalised probabilities
+ * finite), each descale optionally times a factor of its (batch, head)
+ * slice: head_descales is null (per-tensor factors only) or a float32
+ * device array [3][B][H] holding the slices' Q, K and V factors, read by the
+ * kernel (caller-owned; finite and > 0, which the library cannot check before
+ * the launch: other values give non-finite outputs).  Scores accumulate in float32; the unnormalised probabilities
  * P = 2^(s - m_ref) <= 2^tau are rounded to e4m3 (nearest even) before P V;
  * the row sum and LSE use the float32 P.  O is bf16 [B,H,Sq,d], LSE float32
  * [B,H,Sq] (natural log, exact up to float32 rounding of the scores).
@@ -88,8 +92,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  *   arguments and errors as for fa_fwd.  16-byte aligned device pointers.
  * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_descale, float k_descale,
-                     float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal,
-                     float scale, float tau, void* stream);
+                     float v_descale, const float* head_descales, void* O, float* LSE, int B, int H, int Sq,
+                     int Sk, int d, int causal, float scale, float tau, void* stream);
 
 /* Forward over a range of keys, for split-KV and ring (context-parallel)
  * attention: queries i = 0 .. Sq-1 of Q (global index q_offset + i) attend to

@@ -7,7 +7,9 @@ with one dequantisation factor per tensor, so the attention they stand for is
 the ordinary exact attention of the dequantised tensors:
 
   Q = q_descale * e4m3(Q8),  K = k_descale * e4m3(K8),  V = v_descale * e4m3(V8),
-  O, LSE = attention_forward(Q, K, V)   (the definition in ``attention``).
+  O, LSE = attention_forward(Q, K, V)   (the definition in ``attention``),
+
+with each descale one number for the tensor or one per (batch, head) slice.
 
 e4m3 here is the OCP 8-bit format with 4 exponent bits (bias 7), 3 mantissa
 bits, subnormals, no infinities and one NaN pattern per sign (S.1111.111);
@@ -26,9 +28,20 @@ for normal values and 2^-10 below 2^-6; p = exact softmax weights; l_max =
 sum_j exp(s_j - max_j s_j) <= l).  ``fp8_output_bound`` returns that bound
 per element; the LSE is unaffected (the row sum uses the unrounded P).
 
-Pins (tests/test_oracle_fp8.py): the decoder against the format's named
+Accumulating the scores.  The d products of a score are summed in float32;
+the classic summation bound (Higham, Accuracy and Stability of Numerical
+Algorithms, ch. 4) puts the error of a sum of n terms in precision u below
+gamma_n sum |terms|, gamma_n = n u / (1 - n u).  LSE = log sum_j exp(s_j)
+moves by at most the largest score error, so
+``fp8_score_error_bound`` returns gamma_d * scale * max_j sum_c |q_c k_jc|
+per row (visible keys j).  With e4m3 inputs of large magnitude this exceeds
+the float32 LSE tolerance of small-|LSE| rows and is added to it.
+
+Pins (tests/test_oracle_fp8.py): the score bound holds for float32
+sequential and library sums; the decoder against the format's named
 values (0, min subnormal 2^-9, min normal 2^-6, 1, 448, NaN) and against
-torch's float8_e4m3fn on all 256 codes; the bound holds for a brute-force
+torch's float8_e4m3fn on all 256 codes; per-slice descales equal the
+per-tensor form applied slice by slice; the bound holds for a brute-force
 attention that rounds P with torch's e4m3 conversion.
 """
 import numpy as np
@@ -48,7 +61,14 @@ def e4m3_decode(codes):
 
 
 def dequantise(codes, descale):
-    return e4m3_decode(codes) * float(descale)
+    """Values of e4m3 codes [B,H,S,d] times their dequantisation factor: one
+    per tensor (a scalar) or one per (batch, head) slice (an array [B,H])."""
+    f = np.asarray(descale.cpu().numpy() if hasattr(descale, "cpu") else descale, dtype=np.float64)
+    if f.ndim == 2:
+        f = f[:, :, None, None]
+    elif f.ndim != 0:
+        raise ValueError(f"descale must be a scalar or [B,H], got shape {f.shape}")
+    return e4m3_decode(codes) * f
 
 
 def attention_fp8_reference(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
@@ -70,3 +90,18 @@ def fp8_output_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=
     vis = np.tril(np.ones((Sq, Sk))) if causal else np.ones((Sq, Sk))   # visible keys
     absum = np.einsum("ij,bhjc->bhic", vis, av)                          # sum_j |v_j| over them
     return 2.0 ** -4 * rel + 2.0 ** -10 * absum / lmax
+
+
+def fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal=False):
+    """Per-row bound [B,H,Sq] on the float32 accumulation error of the row's
+    scores (and so of its LSE): gamma_d * scale * max over visible keys of
+    sum_c |q_c k_c| on the dequantised inputs (see the module text)."""
+    q, k = np.abs(dequantise(q8, q_descale)), np.abs(dequantise(k8, k_descale))
+    d = q.shape[-1]
+    u = 2.0 ** -24
+    gamma = d * u / (1.0 - d * u)
+    ab = np.einsum("bhic,bhjc->bhij", q, k)
+    if causal:
+        Sq, Sk = ab.shape[-2:]
+        ab = np.where(np.tril(np.ones((Sq, Sk), dtype=bool)), ab, 0.0)
+    return gamma * scale * ab.max(axis=-1)

@@ -60,11 +60,11 @@ def test_fwd_rejects_before_any_launch(L, kw, status):
     assert _fwd(L, **kw) == status
 
 
-def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, B=1, H=1, Sq=16, Sk=16, d=128,
-          causal=0, scale=0.125, tau=8.0):
+def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, hd=0, B=1, H=1, Sq=16, Sk=16,
+          d=128, causal=0, scale=0.125, tau=8.0):
     vp = ctypes.c_void_p
-    return L.fa_fwd_fp8(vp(q), vp(k), vp(v), qs, ks, vs, vp(o), vp(lse), B, H, Sq, Sk, d, causal, scale, tau,
-                        vp(0))
+    return L.fa_fwd_fp8(vp(q), vp(k), vp(v), qs, ks, vs, vp(hd), vp(o), vp(lse), B, H, Sq, Sk, d, causal, scale,
+                        tau, vp(0))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,6 +72,7 @@ def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, B
     (dict(qs=0.0), fa.FA_ERR_INVALID), (dict(vs=-1.0), fa.FA_ERR_INVALID), (dict(ks=float("inf")), fa.FA_ERR_INVALID),
     (dict(tau=8.5), fa.FA_ERR_INVALID), (dict(scale=-1.0), fa.FA_ERR_INVALID), (dict(causal=3), fa.FA_ERR_INVALID),
     (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=8), fa.FA_ERR_UNSUPPORTED),
+    (dict(hd=FAKE + 2), fa.FA_ERR_INVALID), (dict(hd=FAKE + 4, d=64), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_fp8_rejects_before_any_launch(L, kw, status):
     assert _fwd8(L, **kw) == status

@@ -10,9 +10,9 @@ import pytest
 import torch
 
 import exact_attention_50_amd as fa
-from oracle import attention_fp8_reference, e4m3_decode, fp8_output_bound
+from oracle import attention_fp8_reference, e4m3_decode, fp8_output_bound, fp8_score_error_bound
 from parity import LSE_REL, oracle_rows
-from workloads import make_inputs, quantise_e4m3
+from workloads import make_inputs, quantise_e4m3, quantise_e4m3_per_head
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -36,10 +36,13 @@ def run(q8, k8, v8, qs, ks, vs, causal, tau=8.0):
     return o.cpu().double().numpy(), lse.cpu().double().numpy()
 
 
-def check(o, lse, O, L, bound, what):
+def check(o, lse, O, L, bound, what, score_bound=0.0):
+    """O within the P-rounding bound plus the bf16 output rounding; LSE within
+    the forward's relative tolerance plus the float32 accumulation bound of
+    the row's scores (score_bound, oracle.fp8_score_error_bound)."""
     err = np.abs(o - O)
     allowed = bound + 2.0 ** -8 * np.abs(O) + SLACK
-    lse_err = np.abs(lse - L) / np.maximum(1.0, np.abs(L))
+    lse_err = np.maximum(np.abs(lse - L) - score_bound, 0.0) / np.maximum(1.0, np.abs(L))
     stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), bound_max=float(bound.max()),
                  worst_ratio=float((err / allowed).max()), lse_rel=float(lse_err.max()))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
@@ -112,6 +115,30 @@ def test_fp8_extreme_codes_and_zero_queries():
             mean = v[:, :, :n_vis].mean(axis=2)
             assert np.abs(O[:, :, i] - mean).max() < 1e-12
             assert np.abs(L[:, :, i] - math.log(n_vis)).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_per_head_descales_every_element(causal):
+    """Heads of very different magnitudes, each quantised with its own factor
+    (head_descales [3,B,H]); once with per-tensor factors 1, once with
+    per-tensor factors 2, 0.5, 4 and the per-head factors divided by them
+    (the two multiply)."""
+    say(f"fp8 fwd per-head descales B2 H4 S300 causal={causal}")
+    B, H, S, d = 2, 4, 300, 128
+    q, k, v = make_inputs(B, H, S, S, d, seed=47)
+    mag = torch.tensor([1.0, 8.0, 0.125, 2.0]).view(1, H, 1, 1)
+    (q8, qh), (k8, kh), (v8, vh) = (quantise_e4m3_per_head(t.float() * mag) for t in (q, k, v))
+    scale = 1 / math.sqrt(d)
+    O, L = attention_fp8_reference(q8, k8, v8, qh.numpy(), kh.numpy(), vh.numpy(), scale, causal)
+    bound = fp8_output_bound(q8, k8, v8, qh.numpy(), kh.numpy(), vh.numpy(), scale, causal)
+    # head 1 reaches scores of std ~64: float32 accumulation moves small-|LSE| rows
+    sb = fp8_score_error_bound(q8, k8, qh.numpy(), kh.numpy(), scale, causal)
+    for tensor_f in ((1.0, 1.0, 1.0), (2.0, 0.5, 4.0)):
+        hd = torch.stack([qh / tensor_f[0], kh / tensor_f[1], vh / tensor_f[2]]).contiguous().to(DEV)
+        o, lse = fa.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), *tensor_f, causal=causal, head_descales=hd)
+        torch.cuda.synchronize()
+        say(check(o.cpu().double().numpy(), lse.cpu().double().numpy(), O, L, bound,
+                  f"per-head causal={causal} tensor factors {tensor_f}", score_bound=sb))
 
 
 def test_fp8_long_causal_sampled():

@@ -5,7 +5,8 @@ import math
 import numpy as np
 import torch
 
-from oracle import attention_forward, attention_probs, e4m3_decode, fp8_output_bound
+from oracle import (attention_forward, attention_probs, dequantise, e4m3_decode, fp8_output_bound,
+                    fp8_score_error_bound)
 
 
 def test_named_values():
@@ -56,3 +57,44 @@ def test_bound_holds_for_brute_force_rounding_of_p():
         err = np.abs(Oq - O)
         assert np.all(err <= bound * (1 + 1e-9) + 1e-12)
         assert err.max() > 0.05 * bound.max()
+
+
+def test_per_slice_descales_apply_slice_by_slice():
+    """A [B,H] descale scales slice (b, h) -- not a row or a dim -- by its own
+    factor: the result equals the per-tensor form applied to each slice."""
+    g = torch.Generator().manual_seed(9)
+    codes = torch.randint(0, 256, (2, 3, 5, 4), generator=g).to(torch.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                  # no NaN codes
+    f = np.array([[0.5, 2.0, 3.0], [0.25, 8.0, 1.5]])
+    got = dequantise(codes, f)
+    for b in range(2):
+        for h in range(3):
+            assert np.array_equal(got[b, h], dequantise(codes[b:b + 1, h:h + 1], f[b, h])[0, 0])
+    assert np.array_equal(dequantise(codes, 2.0), 2.0 * e4m3_decode(codes))
+
+
+def test_score_bound_holds_for_float32_sums():
+    """Scores summed in float32 -- term by term in order, and by torch's
+    float32 matmul -- differ from the exact ones by no more than
+    fp8_score_error_bound / scale per row; the bound is the worst case (it
+    assumes every rounding error adds up), so a typical error is a small
+    fraction of it, but not a vanishing one."""
+    g = torch.Generator().manual_seed(5)
+    B, H, S, d = 1, 2, 24, 128
+    q8, qs = _quantise(torch.randn(B, H, S, d, generator=g) * 8)
+    k8, ks = _quantise(torch.randn(B, H, S, d, generator=g) * 8)
+    q, k = dequantise(q8, qs), dequantise(k8, ks)
+    exact = np.einsum("bhic,bhjc->bhij", q, k)
+    for causal in (False, True):
+        bound = fp8_score_error_bound(q8, k8, qs, ks, 1.0, causal)
+        seq = np.zeros_like(exact, dtype=np.float32)
+        q32, k32 = q.astype(np.float32), k.astype(np.float32)
+        for c in range(d):
+            seq = (seq + q32[..., :, None, c] * k32[..., None, :, c]).astype(np.float32)
+        lib = torch.from_numpy(q32) @ torch.from_numpy(k32).transpose(-1, -2)
+        vis = np.tril(np.ones((S, S), dtype=bool)) if causal else np.ones((S, S), dtype=bool)
+        for got in (seq.astype(np.float64), lib.double().numpy()):
+            err = np.where(vis, np.abs(got - exact), 0.0).max(axis=-1)
+            assert np.all(err <= bound)
+        err_seq = np.where(vis, np.abs(seq.astype(np.float64) - exact), 0.0).max(axis=-1)
+        assert np.max(err_seq / bound) > 5e-3     # 1.4e-2 here: a worst-case bound

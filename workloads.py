@@ -101,3 +101,12 @@ def quantise_e4m3(x, amax=224.0):
     descale = float(x.abs().max()) / amax if float(x.abs().max()) > 0 else 1.0
     codes = (x.float() / descale).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, descale
+
+
+def quantise_e4m3_per_head(x, amax=224.0):
+    """As quantise_e4m3, with one dequantisation factor per (batch, head)
+    slice of x [B,H,S,d]: returns uint8 codes and float32 factors [B,H]."""
+    m = x.float().abs().amax(dim=(2, 3))
+    descale = torch.where(m > 0, m / amax, torch.ones_like(m))
+    codes = (x.float() / descale[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, descale
