@@ -68,9 +68,8 @@ struct Fwd8Params {
   float tau;
 };
 
+// the 16-byte chunk c of tile row r sits at byte r * kD8 + 16 * (c ^ swz8(r))
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
-// byte offset of chunk c (16 bytes) of row r in a tile
-__device__ __forceinline__ int off8(int r, int c) { return r * kD8 + 16 * (c ^ swz8(r)); }
 
 // e4m3 x e4m3 products written out as single instructions (the compiler
 // moves its own form of this product past barriers to the first use of the
@@ -88,7 +87,6 @@ __device__ __forceinline__ void mfma8_init(f32x16& d, const i32x8& a, const i32x
 __device__ __forceinline__ void drain8(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
-
 
 // k-slot j of lane group g (0, 1) -> key of the 64-key step
 __device__ __forceinline__ int slot_key(int g, int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * g + (j % 4); }
