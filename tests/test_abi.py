@@ -55,6 +55,7 @@ def _fwd(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=16, d=
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=32), fa.FA_ERR_UNSUPPORTED),
     # one head past 31-bit byte offsets: (8M + 1024) rows x 128 dims x 2 bytes
     (dict(d=128, Sq=16, Sk=(1 << 23)), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, Sq=16, Sk=(1 << 31) // 256 - 1024), fa.FA_ERR_UNSUPPORTED),   # one past the largest head
 ])
 def test_fwd_rejects_before_any_launch(L, kw, status):
     assert _fwd(L, **kw) == status

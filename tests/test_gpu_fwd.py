@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import exact_attention_50_amd as fa
-from oracle import attention_forward, conditional_rescale_forward
+from oracle import attention_forward, attention_partial, conditional_rescale_forward, merge_partials
 from parity import check_forward, oracle_rows
 from workloads import WORKLOADS, make_inputs, workload_inputs
 
@@ -181,3 +181,26 @@ def test_exp2_emulation_within_one_bf16_ulp_of_hardware():
     # the hardware exponential against the exact value
     exact = bf16_round(np.exp2(x[:-5].astype(np.float64)).astype(np.float32))
     assert np.mean(bf16_ulp_distance(bf16_round(yh[:-5]), exact) <= 1) == 1.0
+
+
+def test_longest_head_sampled():
+    """The largest head fa_fwd accepts at d = 128 ((Sk + 1024) * d * 2 bytes
+    just under 2^31; one key more is rejected, tests/test_abi.py): 300 queries
+    against 8,387,583 keys, non-causal.  Sampled rows against the oracle's
+    key-range attention over 1M-key chunks, merged by log-sum-exp (the
+    split-KV oracle, pinned to the plain definition)."""
+    d, Sq = 128, 300
+    Sk = (1 << 31) // (d * 2) - 1024 - 1
+    say(f"fwd longest head B1 H1 Sq={Sq} Sk={Sk} d={d}")
+    q, k, v = make_inputs(1, 1, Sq, Sk, d, seed=61)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_fwd(q, k, v, False)
+    rows = [0, 131, 255, 256, 299]
+    qr = q[:, :, rows]
+    parts = [attention_partial(qr, k[:, :, a:a + (1 << 20)], v[:, :, a:a + (1 << 20)], scale, 0, 0,
+                               min(1 << 20, Sk - a))
+             for a in range(0, Sk, 1 << 20)]
+    O, L = merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    st = check_forward(o[:, :, rows], lse[:, :, rows], O, L, "longest head")
+    rel = float(np.max(np.abs(o[:, :, rows].double().numpy() - O)) / np.max(np.abs(O)))
+    say(st, f"O error relative to max|O| = {np.max(np.abs(O)):.3g}: {rel:.3g}")
