@@ -192,3 +192,34 @@ def test_fp8_error_does_not_drift_with_sequence_length():
         say(f"S={S}: kernel error vs dequantised inputs max {e.max():.4g} mean {e.mean():.4g}; "
             f"vs unquantised bf16 inputs max {ei.max():.4g} mean {ei.mean():.4g}")
     assert means[8192] <= 2.0 * means[1024], means
+
+
+def test_fp8_longest_head_sampled():
+    """The largest head the boundary accepts at d = 128 (8,387,583 keys),
+    300 queries, non-causal, e4m3 inputs.  Sampled rows against the oracle's
+    key-range attention of the dequantised inputs over 1M-key chunks, merged
+    by log-sum-exp; the P-rounding bound from the same chunks: sum_j p_j |v_j|
+    is the merged attention of |V|, and l_max = exp(LSE - max_j s_j)."""
+    from oracle import attention_partial, dequantise, merge_partials
+    d, Sq = 128, 300
+    Sk = (1 << 31) // (d * 2) - 1024 - 1
+    say(f"fp8 fwd longest head B1 H1 Sq={Sq} Sk={Sk}")
+    q8, k8, v8, qs, ks, vs = quantised(1, 1, Sq, Sk, d, seed=62)
+    o, lse = run(q8, k8, v8, qs, ks, vs, False)
+    scale = 1 / math.sqrt(d)
+    rows = [0, 131, 255, 256, 299]
+    qq = dequantise(q8[:, :, rows], qs)
+    O_c, L_c, A_c, smax, vabs = [], [], [], -np.inf, 0.0
+    for a in range(0, Sk, 1 << 20):
+        kk, vv = dequantise(k8[:, :, a:a + (1 << 20)], ks), dequantise(v8[:, :, a:a + (1 << 20)], vs)
+        n = kk.shape[2]
+        Oc, Lc = attention_partial(qq, kk, vv, scale, 0, 0, n)
+        Ac, _ = attention_partial(qq, kk, np.abs(vv), scale, 0, 0, n)
+        O_c.append(Oc); L_c.append(Lc); A_c.append(Ac)
+        smax = np.maximum(smax, scale * np.einsum("bhic,bhjc->bhij", qq, kk).max(axis=-1))
+        vabs = vabs + np.abs(vv).sum(axis=2)
+    O, L = merge_partials(np.stack(O_c), np.stack(L_c))
+    A, _ = merge_partials(np.stack(A_c), np.stack(L_c))
+    lmax = np.exp(L - smax)
+    bound = 2.0 ** -4 * A + 2.0 ** -10 * vabs[:, :, None, :] / lmax[..., None]
+    say(check(o[:, :, rows], lse[:, :, rows], O, L, bound, "fp8 longest head"))
