@@ -223,3 +223,31 @@ def test_fp8_longest_head_sampled():
     lmax = np.exp(L - smax)
     bound = 2.0 ** -4 * A + 2.0 ** -10 * vabs[:, :, None, :] / lmax[..., None]
     say(check(o[:, :, rows], lse[:, :, rows], O, L, bound, "fp8 longest head"))
+
+
+def test_fp8_causal_prefix_independence_bitwise():
+    """Causal row i depends on keys 0..i only, bit for bit: replacing every
+    later K and V row by e4m3's largest codes (which raises the row max of
+    the later rows of the same waves, so their rescale branch is taken) leaves
+    rows 0..i of O and LSE unchanged."""
+    say("fp8 fwd causal prefix independence")
+    S, d, i = 320, 128, 150
+    q8, k8, v8, qs, ks, vs = quantised(1, 2, S, S, d, seed=13)
+    o1, l1 = run(q8, k8, v8, qs, ks, vs, True)
+    g = torch.Generator().manual_seed(14)
+    k2, v2 = k8.clone(), v8.clone()
+    sign = torch.randint(0, 2, k2[:, :, i + 1:].shape, generator=g).to(torch.uint8) << 7
+    k2[:, :, i + 1:] = 0x7E | sign                     # +-448
+    v2[:, :, i + 1:] = 0xFE                            # -448
+    o2, l2 = run(q8, k2, v2, qs, ks, vs, True)
+    assert np.array_equal(o1[:, :, :i + 1], o2[:, :, :i + 1])
+    assert np.array_equal(l1[:, :, :i + 1], l2[:, :, :i + 1])
+    assert not np.array_equal(o1[:, :, i + 1:], o2[:, :, i + 1:])
+
+
+def test_fp8_run_to_run_bitwise():
+    say("fp8 fwd run-to-run")
+    q8, k8, v8, qs, ks, vs = quantised(1, 4, 1000, 1000, 128, seed=15)
+    a = run(q8, k8, v8, qs, ks, vs, True)
+    b = run(q8, k8, v8, qs, ks, vs, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
