@@ -4,10 +4,11 @@
 One step = fa_fwd followed by the backward (every step of the forward and
 the backward path) on the bwd workload: B=1, H=16, Sq=Sk=4096, d=128,
 causal, bf16 inputs drawn by workloads.py (seed 5), O and LSE taken from
-fa_fwd.  The backward is enqueued as its three kernels (fa_bwd_phase with
-PREPARE, DQ, DKDV: the same launches fa_bwd makes) with HIP events between
-them, on the stream the kernels run on, so each kernel's average duration is
-measured inside the timed region.  Inputs and outputs are resident in device
+fa_fwd.  The backward is enqueued as its two launches (fa_bwd_phase with
+PREPARE | DQ, whose dQ kernel also forms the row terms, then DKDV: the same
+launches fa_bwd makes) with HIP events between them, on the stream the
+kernels run on, so each kernel's average duration is measured inside the
+timed region.  Inputs and outputs are resident in device
 memory before timing starts.
 
 Printed: ONE JSON line with the throughput in TFLOP/s (counted FLOPs:
@@ -227,11 +228,11 @@ def main():
         fa.fa_bwd_phase(ph, q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
                         deterministic=bool(args.deterministic))
 
-    # the step, kernel by kernel (fa_bwd = the three phases in this order)
+    # the step, kernel by kernel, as fa_bwd launches it: PREPARE and DQ in one
+    # call (the dQ kernel forms the row terms D_i, LSE_i log2(e) itself), then DKDV
     parts = [("fwd_kernel", fwd)]
     if do_bwd:
-        parts += [("bwd_prep_kernel", lambda: bwd_phase(fa.FA_BWD_PREPARE)),
-                  ("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_DQ)),
+        parts += [("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_PREPARE | fa.FA_BWD_DQ)),
                   ("bwd_dkdv_kernel", lambda: bwd_phase(fa.FA_BWD_DKDV))]
 
     # ---- clock warm-up and W warmup steps, then exactly K timed steps with
@@ -258,16 +259,14 @@ def main():
     step_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
 
     # counted FLOPs (the configs' convention) and each kernel's own algorithmic
-    # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ); dK/dV
-    # kernel 8d (S, dP, dV, dK); prep: HBM bytes (read O, dO and LSE, write D
-    # and LSE log2(e))
+    # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ; its row
+    # terms are O(rows d) beside them); dK/dV kernel 8d (S, dP, dV, dK)
     pairs = w.flops("fwd") / (4 * d)
     f_fwd = w.flops("fwd")
     f_bwd = w.flops("bwd") if do_bwd else 0.0
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
     work = {"fwd_kernel": ("mfma", 4 * d * pairs), "bwd_dq_kernel": ("mfma", 6 * d * pairs),
-            "bwd_dkdv_kernel": ("mfma", 8 * d * pairs),
-            "bwd_prep_kernel": ("hbm", B * H * Sq * (2 * d * 2 + 3 * 4))}
+            "bwd_dkdv_kernel": ("mfma", 8 * d * pairs)}
     kernels = {}
     for (name, _), ms in zip(parts, part_ms):
         bound, amount = work[name]

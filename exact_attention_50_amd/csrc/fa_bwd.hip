@@ -12,7 +12,7 @@
 // MI355X fp32 atomics to one accumulator from many XCDs run at ~1 TB/s, and
 // ordering them serialises the key blocks of a head.  Here the backward is
 // split by output instead, so every output element is written exactly once:
-//   bwd_prep_kernel   D_i;
+//   bwd_prep_kernel   D_i (inside bwd_dq_kernel when both run in one call);
 //   bwd_dq_kernel     a workgroup owns 256 query rows and streams K / V tiles:
 //                     S^T = K Q^T, dP^T = V dO^T (one query per lane, so LSE_i
 //                     and D_i are per-lane scalars), dS^T, dQ^T += K^T dS^T;
@@ -47,6 +47,7 @@ struct BwdParams {
   float* dvec;   // D_i, [B, H, Sq]
   float* lse2;   // LSE_i * log2(e), [B, H, Sq]
   int BH, Sq, Sk;
+  int fuse_prep; // the dQ kernel forms D_i and LSE_i log2(e) itself and stores them
   float scale;
   float scale_log2;
 };
@@ -151,18 +152,47 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int tr_lane = tr_lane_offset<D>(lane);
 
   // B operands: the lane's Q and dO rows, dims 16 kc + 8 g .. +8 (AGPRs)
+  const bool fuse = p.fuse_prep != 0;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + (size_t)bh * p.Sq * D, head_q);
   bf16x8 qf[kKC], of[kKC];
+  float dchunk[kKC];   // sum over the 8 dims 16 kc + 8 g .. of dO O (fused prep only)
 #pragma unroll
   for (int kc = 0; kc < kKC; ++kc) {
     const unsigned off = (unsigned)qi * G::kRowBytes + (kc * 16 + 8 * g) * 2;
     qf[kc] = __builtin_bit_cast(bf16x8, load16(rq, off));
     of[kc] = __builtin_bit_cast(bf16x8, load16(rdo, off));
+    dchunk[kc] = 0.0f;
+    if (fuse) {
+      const bf16x8 oc = __builtin_bit_cast(bf16x8, load16(ro, off));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dchunk[kc] = __builtin_fmaf((float)oc[j], (float)of[kc][j], dchunk[kc]);
+    }
     asm volatile("s_nop 1" : "+a"(qf[kc]), "+a"(of[kc]));
   }
   // the lane's row terms (rows past the end: any finite value; never stored)
   const size_t ri = (size_t)bh * p.Sq + (q_ok ? qi : 0);
-  const float lse2 = p.lse2[ri];
-  const float dval = p.dvec[ri];
+  float lse2, dval;
+  if (fuse) {
+    // D_i in the association of bwd_prep_kernel's butterfly (16 lanes of 8
+    // dims at D = 128, 8 at D = 64; its lane 0 ends with the even 8-dim
+    // chunks plus the odd ones), so the value is bit-identical: here chunk
+    // 2 kc + g sits in lane g of the pair
+    static_assert(kKC == 8 || kKC == 4, "D = 128 or 64");
+    float w;
+    if constexpr (kKC == 8)
+      w = ((dchunk[0] + dchunk[4]) + (dchunk[2] + dchunk[6])) + ((dchunk[1] + dchunk[5]) + (dchunk[3] + dchunk[7]));
+    else
+      w = (dchunk[0] + dchunk[2]) + (dchunk[1] + dchunk[3]);
+    dval = w + __shfl_xor(w, 32);
+    lse2 = p.lse[ri] * kLog2e;
+    if (q_ok && g == 0) {
+      p.dvec[ri] = dval;
+      p.lse2[ri] = lse2;
+    }
+  } else {
+    lse2 = p.lse2[ri];
+    dval = p.dvec[ri];
+  }
 
   f32x16 dq[kDB];
 #pragma unroll
@@ -661,7 +691,11 @@ hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t 
   prm.dvec = static_cast<float*>(a.workspace);
   prm.lse2 = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + sec);
   hipError_t e = hipSuccess;
-  if (phases & kBwdPrepare) {
+  // PREPARE and DQ in one call: the dQ kernel forms the row terms of its own
+  // rows (bit-identical to the prep kernel's) and stores them for DKDV
+  const bool fuse = (phases & kBwdPrepare) && (phases & kBwdDq);
+  prm.fuse_prep = fuse ? 1 : 0;
+  if ((phases & kBwdPrepare) && !fuse) {
     const long long rows = (long long)a.B * a.H * a.Sq;
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(1024), dim3(256), 0, stream, prm, rows);
     e = hipGetLastError();

@@ -157,15 +157,18 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* The three kernels of fa_bwd, enqueued separately (a bit mask, executed in
+/* The three parts of fa_bwd, enqueued separately (a bit mask, executed in
  * this order within one call):
  *   FA_BWD_PREPARE  D_i = sum_c dO_ic O_ic and LSE_i log2(e) into the
  *                   workspace;
  *   FA_BWD_DQ       dQ (reads the row terms; writes dQ only);
  *   FA_BWD_DKDV     dK and dV (reads the row terms; writes dK, dV only).
- * After PREPARE has completed, DQ and DKDV are independent and may run on
- * different streams (the caller orders them with events).  Arguments and
- * validation are those of fa_bwd; fa_bwd is fa_bwd_phase(FA_BWD_ALL, ...). */
+ * PREPARE and DQ in the same call run as one launch: the dQ kernel forms the
+ * row terms of its rows itself (bit-identical to PREPARE's) and stores them
+ * in the workspace before DKDV reads them.  After a PREPARE call has
+ * completed, DQ and DKDV are independent and may run on different streams
+ * (the caller orders them with events).  Arguments and validation are those
+ * of fa_bwd; fa_bwd is fa_bwd_phase(FA_BWD_ALL, ...). */
 #define FA_BWD_PREPARE 1
 #define FA_BWD_DQ 2
 #define FA_BWD_DKDV 4

@@ -97,15 +97,25 @@ def test_workspace_reuse_and_dirty_workspace():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
 def test_phases_separately_equal_fa_bwd(d, causal):
     """fa_bwd_phase(PREPARE), then DQ, then DKDV (also DKDV before DQ) writes
-    the same bits as one fa_bwd call; DQ and DKDV each touch only their outputs."""
+    the same bits as one fa_bwd call, which forms the row terms inside the dQ
+    kernel (workspace included); DQ and DKDV each touch only their outputs."""
     say(f"bwd phases d={d} causal={causal}")
     q, k, v, do = (t.to(DEV) for t in make_inputs(1, 3, 333, 333, d, seed=40 + d, with_dout=True))
     o, lse = fa.forward(q, k, v, causal=causal)
     ref = fa.backward(q, k, v, o, lse, do, causal=causal)
     nbytes = fa.fa_bwd_workspace_bytes(1, 3, 333, 333, d, causal, False)
+    ws_fused = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    fused = [torch.empty_like(q) for _ in range(3)]
+    fa.fa_bwd(q, k, v, o, lse, do, *fused, ws_fused, causal=causal)
+    ws_prep = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_phase(fa.FA_BWD_PREPARE, q, k, v, o, lse, do, *fused, ws_prep, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(ws_fused, ws_prep), "row terms of the fused dQ kernel differ from the prep kernel's"
+    for a, b in zip(fused, ref):
+        assert torch.equal(a, b)
     for order in ((fa.FA_BWD_DQ, fa.FA_BWD_DKDV), (fa.FA_BWD_DKDV, fa.FA_BWD_DQ)):
         ws = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
         outs = [torch.full_like(q, 7.0) for _ in range(3)]
