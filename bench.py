@@ -312,6 +312,16 @@ def main():
                 extra[f"{ww.name}-fp8"] = {
                     "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3",
                     "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
+                if wid == 3:
+                    # ablation of the conditional rescale where the softmax's VALU
+                    # work is the bound: tau = 0 corrects on every rise of a row max
+                    ms = time_calls(lambda: fa.fa_fwd_fp8(q8, k8, v8, oo, ll, qs, ks, vs, causal=ww.causal,
+                                                          scale=ww.scale, tau=0.0),
+                                    max(10, args.steps), 3, args.warm_seconds / 3)
+                    tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                    extra[f"{ww.name}-fp8-tau0"] = {
+                        "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3", "tau": 0.0,
+                        "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
                 del q8, k8, v8
             if wid == 4:
                 # ablation of the conditional rescale: tau = 0 corrects the
