@@ -14,7 +14,7 @@ import math
 import os
 
 __all__ = [
-    "FAError", "lib", "fa_fwd", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
+    "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
     "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
     "backward", "LIB_PATH",
 ]
@@ -45,6 +45,8 @@ def lib():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_rescale_count.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp, vp]
+    L.fa_fwd_rescale_count.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
@@ -118,6 +120,29 @@ def fa_fwd(q, k, v, o, lse, causal=False, scale=None, tau=8.0, emu_frac=0.0):
                       float(scale), float(tau), float(emu_frac), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
+
+
+def fa_fwd_rescale_count(q, k, v, o, lse, events, causal=False, scale=None, tau=8.0):
+    """The instrumented forward (hardware exponentials): fills o and lse as
+    fa_fwd does and adds, per (b, h), the wavefront-level corrections taken
+    after each wavefront's first key tile to events (int32 CUDA [B, H])."""
+    import torch
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    _check_bf16("q", q, (B, H, Sq, d))
+    _check_bf16("k", k, (B, H, Sk, d))
+    _check_bf16("v", v, (B, H, Sk, d))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    if events.dtype != torch.int32 or not events.is_cuda or not events.is_contiguous() or \
+            tuple(events.shape) != (B, H):
+        raise ValueError(f"events: expected a contiguous int32 CUDA tensor of shape {(B, H)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_rescale_count(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,
+                                    int(bool(causal)), float(scale), float(tau), _ptr(events), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_rescale_count")
 
 
 def _check_e4m3(name, t, shape):

@@ -1,6 +1,7 @@
 // C ABI of the attention library: argument validation, then one launch
 // sequence on the caller's stream.  Declarations and contracts: include/fa.h.
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -71,6 +72,33 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_rescale_count(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                int Sq, int Sk, int d, int causal, float scale, float tau, unsigned int* events,
+                                void* stream) {
+  if (!events || (reinterpret_cast<uintptr_t>(events) & 3u) != 0) return FA_ERR_INVALID;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 64.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.q_off = 0; a.k_begin = 0; a.k_end = Sk;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.tau = tau;
+  a.emu_count = 0;
+  a.events = events;
+  const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_descale, float k_descale,
                      float v_descale, const float* head_descales, void* O, float* LSE, int B, int H, int Sq, int Sk,
                      int d, int causal, float scale, float tau, void* stream) {
@@ -81,6 +109,11 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
   if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
   for (float f : {q_descale, k_descale, v_descale})
     if (!(isfinite(f) && f > 0.0f)) return FA_ERR_INVALID;
+  // the kernel folds the score factors into one float: it must stay a
+  // finite normal number (each factor alone can pass while the product
+  // overflows or underflows)
+  const float score_factor = scale * q_descale * k_descale * 1.4426950408889634f;
+  if (!(isfinite(score_factor) && score_factor >= FLT_MIN)) return FA_ERR_INVALID;
   if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
@@ -113,7 +146,9 @@ fa_status fa_fwd_partial(const void* Q, const void* K, const void* V, float* O_p
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
   if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
-  if ((long long)q_offset + Sq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  // the kernel forms causal bounds as q_offset + (row block end) + (one
+  // tile) in 32-bit ints, up to q_offset + Sq + 414
+  if ((long long)q_offset + Sq + 512 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdArgs a;
   a.q = Q; a.k = K; a.v = V; a.o = nullptr; a.o32 = O_part; a.lse = LSE_part;

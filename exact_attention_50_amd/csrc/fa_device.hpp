@@ -195,6 +195,25 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand of v_mfma_f32_16x16x32_bf16 that turns it into per-query row
+// sums of a 32x32x16 B operand (lane l = 32 g + r holding 8 values of query r).
+// In the 16x16x32 product lane l supplies A row l % 16 at k-group l / 16 and
+// B column l % 16 at k-group l / 16; the B k-groups 0 and 2 (lanes 0-15,
+// 32-47) hold queries c = l % 16, groups 1 and 3 hold queries c + 16.  Row 0
+// of the selector is one on groups 0 and 2, row 1 on groups 1 and 3, all
+// other rows zero, so C[0][c] and C[1][c] (lane c < 16, elements 0 and 1)
+// collect the sums of queries c and c + 16 and every other element stays 0.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  const int row = lane & 15, kg = lane >> 4;
+  const bool one = (row == 0 && (kg & 1) == 0) || (row == 1 && (kg & 1) == 1);
+  const __bf16 v = one ? (__bf16)1.0f : (__bf16)0.0f;
+  return bf16x8{v, v, v, v, v, v, v, v};
+}
+
 // Round eight floats to bf16 (nearest-even) and pack them as an MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
                                               float a6, float a7) {

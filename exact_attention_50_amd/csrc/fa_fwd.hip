@@ -72,6 +72,7 @@ struct FwdParams {
   int n_qblocks;
   float scale_log2;  // scale * log2(e)
   float tau;
+  unsigned* events;  // counting instantiation: corrections per (b, h), added to
 };
 
 // LDS of the 256-row form: K ring of 2 stages, then V ring of 2 stages, each
@@ -99,7 +100,10 @@ constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
 // end.  Twice as many workgroups of half the size let the scheduler pair
 // heavy causal blocks with light ones when one 256-row block per CU would
 // leave the chip waiting on the heaviest.
-template <int D, bool CAUSAL, int EMU, bool SPLIT>
+// COUNT: the instrumented instantiation adds, per (b, h), the number of
+// (wavefront, tile) steps after the wavefront's first tile in which the
+// correction branch was taken to p.events.
+template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT = false>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   using L = FwdLayout<D, SPLIT>;
   constexpr int kBN = L::kBN;
@@ -185,7 +189,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   f32x16 s[kKB];
   bf16x8 pk[kKS];
   float m_ref = kNegInf;
-  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // 4 partial row sums
+  float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // 4 partial row sums of the float32 P (for the LSE)
+  // Row sums of the bf16 weights P V multiplies (for O), on the matrix pipe:
+  // a 16x16x32 product of a 0/1 selector with the packed P^T of a 16-key step
+  // adds the step's 16 weights of query c to C[0][c] and of query c + 16 to
+  // C[1][c] (lane c < 16 holds both).  O divided by this sum is a weighted
+  // mean of V rows, so a row that one key dominates gets that key's V row
+  // unchanged; a division by the float32 sum would carry the bf16 rounding of
+  // the dominant weight into O.
+  f32x4 lh4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8 lh_sel = row_sum_selector(lane);
+  int n_events = 0;                             // COUNT only (wave-uniform)
 
   // ---- matrix phase: O += V_{t-1} P_{t-1}, then S_t = K_t Q^T, as one stream
   // of MFMAs whose LDS operands are read kAhead MFMAs ahead through a small
@@ -220,6 +234,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       if (j + kAhead < j1) ring[(j - j0) % kAhead] = operand(j + kAhead);
       if (j < kNV) {
         o[j % kDB] = mfma32x32x16(a, pk[j / kDB], o[j % kDB]);
+        // the row sum of exactly the bf16 weights P V multiplies, on VALU
+        // slots the matrix phase leaves idle: O divided by it is a weighted
+        // mean of V rows, so a row that one key dominates gets that key's V
+        // row unchanged (a division by the float32 sum would carry the bf16
+        // rounding of that key's weight)
+        if (j % kDB == kDB - 1) lh4 = mfma16x16x32(lh_sel, pk[j / kDB], lh4);
       } else {
         const int i = j - kNV;
         s[i % kKB] = mfma32x32x16(a, qf[i / kKB], s[i % kKB]);
@@ -285,9 +305,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     // more than tau move their reference, the others multiply by exactly 1
     const bool need = (m_new - m_ref) > p.tau;   // first tile: +inf > tau
     if (__any(need)) {
+      if constexpr (COUNT) n_events += t > 0 ? 1 : 0;
       const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;   // exp2(-inf) = 0
 #pragma unroll
       for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
+      // the selector sums hold queries lane % 16 and lane % 16 + 16
+      lh4[0] *= __shfl(alpha, lane & 15);
+      lh4[1] *= __shfl(alpha, (lane & 15) + 16);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
       m_ref = need ? m_new : m_ref;
@@ -479,12 +503,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       }
     }
   }
+  if constexpr (COUNT) {
+    // one vector atomic per wavefront (lane 0 holds the address)
+    if (lane == 0 && n_events > 0) atomicAdd(p.events + bh, (unsigned)n_events);
+  }
   float l_lane = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
+  // this lane's query r32 from lane r32 % 16 (row 0: queries 0-15, row 1: 16-31)
+  float lh_lane;
+  {
+    const float x0 = __shfl(lh4[0], r32 & 15), x1 = __shfl(lh4[1], r32 & 15);
+    lh_lane = r32 < 16 ? x0 : x1;
+  }
   if constexpr (SPLIT) {
-    // group 1 hands (O, row sum, reference max) of each lane to the lane of
+    // group 1 hands (O, row sums, reference max) of each lane to the lane of
     // group 0 that holds the same row and columns; the ring is idle now
     constexpr int kXO = kDB * 4 * 256 * 16;   // O: [db * 4 + i4][256 lanes] f32x4
-    static_assert(kXO + 2 * 256 * 4 <= L::kLdsBytes, "merge area exceeds the LDS ring");
+    static_assert(kXO + 3 * 256 * 4 <= L::kLdsBytes, "merge area exceeds the LDS ring");
     const int tl = (wave & 3) * 64 + lane;
     f32x4* xo = reinterpret_cast<f32x4*>(smem);
     float* xs = reinterpret_cast<float*>(smem + kXO);
@@ -497,6 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
                                                o[db][4 * i4 + 3]};
       xs[tl] = m_ref;
       xs[256 + tl] = l_lane;
+      xs[512 + tl] = lh_lane;
     }
     barrier();
     if (group == 1) return;
@@ -506,6 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const float a0 = (m_ref == kNegInf) ? 0.0f : exp2_hw(m_ref - m);
     const float a1 = (m1 == kNegInf) ? 0.0f : exp2_hw(m1 - m);
     l_lane = l_lane * a0 + xs[256 + tl] * a1;
+    lh_lane = lh_lane * a0 + xs[512 + tl] * a1;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -517,19 +553,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     m_ref = m;
   }
 
-  // ---- epilogue: O = O / l (bf16 or float32), LSE = (m_ref + log2 l) ln 2;
-  // a row that saw no key (only possible for a key range) gets O = 0 and
-  // LSE = -inf, the identity of the merge of partial results
+  // ---- epilogue: O = O / lh (bf16 or float32; lh sums the bf16 weights P V
+  // used), LSE = (m_ref + log2 l) ln 2 (l sums the float32 P); a row that saw
+  // no key (only possible for a key range) gets O = 0 and LSE = -inf, the
+  // identity of the merge of partial results
   const float l = pair_sum(l_lane);
+  const float lh = lh_lane;   // already the whole row's sum (both lane halves)
   const bool empty = !(l > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l;
+  const float inv_l = empty ? 0.0f : 1.0f / lh;
   if (!p.o32) {
     // bf16 output, stored as whole rows through a per-wave LDS area in the
     // ring, idle after the last barrier (every tile read and load has
     // completed); in the split form the areas follow the merge area, which
     // the other waves of group 0 may still be reading
     using RS = RowStore<D>;
-    constexpr int kStageBase = SPLIT ? kDB * 4 * 256 * 16 + 2 * 256 * 4 : 0;
+    constexpr int kStageBase = SPLIT ? kDB * 4 * 256 * 16 + 3 * 256 * 4 : 0;
     constexpr int kStagingWaves = SPLIT ? kWaves / 2 : kWaves;
     static_assert(kStageBase + kStagingWaves * RS::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
     RS::store(smem + kStageBase + (SPLIT ? (wave & 3) : wave) * RS::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * D,
@@ -554,9 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 // instantiated.
 constexpr int kEmuCounts[] = {0, 3, 8, 16, 32};
 
-template <int D, bool CAUSAL, int EMU, bool SPLIT>
+template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT = false>
 hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
-  auto kern = fwd_kernel<D, CAUSAL, EMU, SPLIT>;
+  auto kern = fwd_kernel<D, CAUSAL, EMU, SPLIT, COUNT>;
   const int lds = FwdLayout<D, SPLIT>::kLdsBytes;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -567,6 +605,7 @@ hipError_t launch_one(const FwdParams& prm, dim3 grid, hipStream_t stream) {
 
 template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_d_causal(const FwdParams& prm, int emu, dim3 grid, hipStream_t stream) {
+  if (prm.events) return launch_one<D, CAUSAL, 0, SPLIT, true>(prm, grid, stream);
   switch (emu) {
     case 0: return launch_one<D, CAUSAL, 0, SPLIT>(prm, grid, stream);
     case 3: return launch_one<D, CAUSAL, 3, SPLIT>(prm, grid, stream);
@@ -613,6 +652,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   prm.q_off = a.q_off;
   prm.scale_log2 = a.scale * kLog2e;
   prm.tau = a.tau;
+  prm.events = a.events;
+  if (a.events && a.emu_count != 0) return hipErrorInvalidValue;   // counted with hardware exponentials only
   const long long full_blocks = (long long)((a.Sq + kBM - 1) / kBM) * prm.BH;
   const bool split = a.causal && full_blocks < kSplitBelowBlocks;
   const int rows = split ? kBM / 2 : kBM;

@@ -21,6 +21,8 @@ struct FwdArgs {
   float scale;
   float tau;
   int emu_count;  // exponentials per lane per tile computed in software
+  unsigned* events = nullptr;   // non-null: the instrumented instantiation, which
+                                // adds its correction counts per (b, h) here
 };
 
 // Exponentials of one lane per 64 keys (64 keys x 32 queries / 64 lanes): the

@@ -45,7 +45,8 @@ from .online_softmax import conditional_rescale_forward
 from .exp2_emulation import (fit_exp2_minimax, exp2_emulated_f32, bf16_round,
                              bf16_ulp_distance, relative_error_curve)
 from .partial import attention_partial, merge_partials
-from .fp8 import e4m3_decode, dequantise, attention_fp8_reference, fp8_output_bound, fp8_score_error_bound
+from .fp8 import (e4m3_decode, dequantise, attention_fp8_reference, fp8_output_bound, fp8_score_error_bound,
+                  fp8_float32_bound, summation_gamma)
 from . import roofline
 
 __all__ = [
@@ -54,4 +55,5 @@ __all__ = [
     "fit_exp2_minimax", "exp2_emulated_f32", "bf16_round", "bf16_ulp_distance",
     "relative_error_curve", "attention_partial", "merge_partials", "roofline",
     "e4m3_decode", "dequantise", "attention_fp8_reference", "fp8_output_bound", "fp8_score_error_bound",
+    "fp8_float32_bound", "summation_gamma",
 ]

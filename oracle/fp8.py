@@ -37,12 +37,40 @@ moves by at most the largest score error, so
 per row (visible keys j).  With e4m3 inputs of large magnitude this exceeds
 the float32 LSE tolerance of small-|LSE| rows and is added to it.
 
+Float32 arithmetic on O.  Beside rounding P, the kernel's O moves by the
+float32 arithmetic of its steps; ``fp8_float32_bound`` bounds that per
+element by
+
+  [ expm1(2 eps) + 2 g_n + 16 u ] * sum_j p_j |v_j|
+
+with u = 2^-24, n = the row's visible keys and
+  * eps = the score error of the row (``fp8_score_error_bound``) plus
+    8 u max_j |s_j|: the folded score factor (three roundings), the
+    scale-and-subtract FMA; a score error delta_j changes the weight p_j by
+    at most a factor exp(+-2 max|delta|) after normalisation;
+  * g_n for each of the two sums over the keys, the numerator sum_j P_j v_j
+    and the row sum l (each term passes through at most n - 1 roundings,
+    in any summation order or blocking): the smaller of the worst case
+    gamma_n = n u / (1 - n u) and the probabilistic bound of Higham and Mary
+    ("A New Approach to Probabilistic Rounding Error Analysis", SIAM J. Sci.
+    Comput. 41(5), 2019, Theorem 2.4 and its summation corollary):
+    exp(lambda sqrt(n) u + n u^2 / (1 - u)) - 1, which holds with
+    probability at least 1 - 2 n exp(-lambda^2 (1 - u)^2 / 2) when the
+    rounding errors are independent and of mean zero; lambda = 10 puts the
+    failure probability below n * 4e-22.  For the 8.4 M-key rows the worst
+    case is vacuous (n u = 0.5) and the probabilistic bound 1.7e-3;
+  * 16 u for the fixed number of roundings per element: the exponential
+    (within one ulp), the rescale and final 1/l multiplies.
+The bf16 rounding of the output is a separate term of the tests (2^-8 |O|).
+
 Pins (tests/test_oracle_fp8.py): the score bound holds for float32
 sequential and library sums; the decoder against the format's named
 values (0, min subnormal 2^-9, min normal 2^-6, 1, 448, NaN) and against
 torch's float8_e4m3fn on all 256 codes; per-slice descales equal the
 per-tensor form applied slice by slice; the bound holds for a brute-force
-attention that rounds P with torch's e4m3 conversion.
+attention that rounds P with torch's e4m3 conversion; the summation bound
+holds for float32 sums (sequential, pairwise and library) of up to 4 M
+terms and is within 50x of their actual error (not vacuous).
 """
 import numpy as np
 
@@ -105,3 +133,32 @@ def fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal=False):
         Sq, Sk = ab.shape[-2:]
         ab = np.where(np.tril(np.ones((Sq, Sk), dtype=bool)), ab, 0.0)
     return gamma * scale * ab.max(axis=-1)
+
+
+U32 = 2.0 ** -24
+
+
+def summation_gamma(n, lam=10.0):
+    """Relative error bound of a float32 sum of n terms, relative to
+    sum |terms| (see the module text): min(worst case, probabilistic)."""
+    n = np.asarray(n, dtype=np.float64)
+    nu = n * U32
+    worst = np.where(nu < 1.0, nu / np.maximum(1.0 - nu, 1e-300), np.inf)
+    prob = np.expm1(lam * np.sqrt(n) * U32 + n * U32 * U32 / (1.0 - U32))
+    return np.minimum(worst, prob)
+
+
+def fp8_float32_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
+    """Per-element bound [B,H,Sq,d] on what float32 arithmetic adds to the
+    kernel's O error beside the rounding of P (see the module text)."""
+    q, k, v = dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale)
+    p = attention_probs(q, k, scale, causal)
+    rel = np.einsum("bhij,bhjc->bhic", p, np.abs(_f64(v)))        # sum_j p_j |v_j|
+    Sq, Sk = p.shape[-2], p.shape[-1]
+    vis = np.tril(np.ones((Sq, Sk), dtype=bool)) if causal else np.ones((Sq, Sk), dtype=bool)
+    s_abs = np.abs(scale * np.einsum("bhic,bhjc->bhij", _f64(q), _f64(k)))
+    smax = np.where(vis, s_abs, 0.0).max(axis=-1)
+    eps = fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal) + 8.0 * U32 * smax
+    n = vis.sum(axis=-1).astype(np.float64)                          # [Sq]
+    factor = np.expm1(2.0 * eps) + 2.0 * summation_gamma(n) + 16.0 * U32
+    return factor[..., None] * rel

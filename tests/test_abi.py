@@ -74,6 +74,9 @@ def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, h
     (dict(tau=8.5), fa.FA_ERR_INVALID), (dict(scale=-1.0), fa.FA_ERR_INVALID), (dict(causal=3), fa.FA_ERR_INVALID),
     (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=8), fa.FA_ERR_UNSUPPORTED),
     (dict(hd=FAKE + 2), fa.FA_ERR_INVALID), (dict(hd=FAKE + 4, d=64), fa.FA_ERR_UNSUPPORTED),
+    # each factor valid on its own, their product (folded into one float
+    # score factor) overflows or underflows
+    (dict(qs=1e30, ks=1e30), fa.FA_ERR_INVALID), (dict(qs=1e-30, ks=1e-20), fa.FA_ERR_INVALID),
 ])
 def test_fwd_fp8_rejects_before_any_launch(L, kw, status):
     assert _fwd8(L, **kw) == status
@@ -96,6 +99,10 @@ def test_partial_and_merge_validation(L):
     assert part(o=0) == fa.FA_ERR_INVALID
     assert part(causal=2) == fa.FA_ERR_INVALID
     assert part(d=80) == fa.FA_ERR_UNSUPPORTED
+    # causal bounds are formed as q_offset + row block end + one tile in
+    # 32-bit ints: offsets that would overflow them are refused
+    assert part(q_off=(1 << 31) - 16 - 512) == fa.FA_ERR_UNSUPPORTED
+    assert part(q_off=(1 << 31) - 16 - 1, causal=1) == fa.FA_ERR_UNSUPPORTED
 
     def merge(**kw):
         a = dict(op=FAKE, lp=FAKE, n=2, B=1, H=1, Sq=16, d=64, o=FAKE, lse=FAKE)

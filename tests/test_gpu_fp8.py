@@ -10,13 +10,13 @@ import pytest
 import torch
 
 import exact_attention_50_amd as fa
-from oracle import attention_fp8_reference, e4m3_decode, fp8_output_bound, fp8_score_error_bound
+from oracle import (attention_fp8_reference, e4m3_decode, fp8_float32_bound, fp8_output_bound,
+                    fp8_score_error_bound, summation_gamma)
 from parity import LSE_REL, oracle_rows
 from workloads import make_inputs, quantise_e4m3, quantise_e4m3_per_head
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SLACK = 2e-3   # float32 accumulation and exponentials, far below the bound
 
 
 def say(*a):
@@ -36,12 +36,26 @@ def run(q8, k8, v8, qs, ks, vs, causal, tau=8.0):
     return o.cpu().double().numpy(), lse.cpu().double().numpy()
 
 
+def bounds(q8, k8, v8, qs, ks, vs, scale, causal):
+    """Per-element bound of the kernel's O error: rounding P to e4m3 plus the
+    float32 arithmetic (oracle.fp8_output_bound + oracle.fp8_float32_bound)."""
+    return (fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+            + fp8_float32_bound(q8, k8, v8, qs, ks, vs, scale, causal))
+
+
+def row_bounds(q8, k8, v8, qs, ks, vs, scale, b, h, rows):
+    """bounds() of causal rows i of slice (b, h), each on its key prefix."""
+    return np.stack([bounds(q8[b:b + 1, h:h + 1, i:i + 1], k8[b:b + 1, h:h + 1, :i + 1],
+                            v8[b:b + 1, h:h + 1, :i + 1], qs, ks, vs, scale, False)[0, 0, 0] for i in rows])
+
+
 def check(o, lse, O, L, bound, what, score_bound=0.0):
-    """O within the P-rounding bound plus the bf16 output rounding; LSE within
-    the forward's relative tolerance plus the float32 accumulation bound of
-    the row's scores (score_bound, oracle.fp8_score_error_bound)."""
+    """O within the bound of rounding P plus the float32 arithmetic (bound)
+    plus the bf16 output rounding; LSE within the forward's relative tolerance
+    plus the float32 accumulation bound of the row's scores (score_bound,
+    oracle.fp8_score_error_bound)."""
     err = np.abs(o - O)
-    allowed = bound + 2.0 ** -8 * np.abs(O) + SLACK
+    allowed = bound + 2.0 ** -8 * np.abs(O)
     lse_err = np.maximum(np.abs(lse - L) - score_bound, 0.0) / np.maximum(1.0, np.abs(L))
     stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), bound_max=float(bound.max()),
                  worst_ratio=float((err / allowed).max()), lse_rel=float(lse_err.max()))
@@ -60,7 +74,7 @@ def test_fp8_small_shapes_every_element(Sq, Sk, causal):
     o, lse = run(q8, k8, v8, qs, ks, vs, causal)
     scale = 1 / math.sqrt(d)
     O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, causal)
-    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+    bound = bounds(q8, k8, v8, qs, ks, vs, scale, causal)
     say(check(o, lse, O, L, bound, f"{Sq}x{Sk} c{causal}"))
 
 
@@ -73,7 +87,7 @@ def test_fp8_many_heads_every_element(tau):
     o, lse = run(q8, k8, v8, qs, ks, vs, True, tau=tau)
     scale = 1 / math.sqrt(d)
     O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
-    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, True)
+    bound = bounds(q8, k8, v8, qs, ks, vs, scale, True)
     say(check(o, lse, O, L, bound, f"H64 S1000 tau={tau}"))
 
 
@@ -89,7 +103,7 @@ def test_fp8_key_ramp_every_element(tau):
     o, lse = run(q8, k8, v8, qs, ks, vs, True, tau=tau)
     scale = 1 / math.sqrt(d)
     O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
-    bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, True)
+    bound = bounds(q8, k8, v8, qs, ks, vs, scale, True)
     say(check(o, lse, O, L, bound, f"ramp tau={tau}"))
 
 
@@ -106,7 +120,7 @@ def test_fp8_extreme_codes_and_zero_queries():
     for causal in (False, True):
         o, lse = run(q8, k8, v8, qs, ks, vs, causal)
         O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, causal)
-        bound = fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+        bound = bounds(q8, k8, v8, qs, ks, vs, scale, causal)
         say(check(o, lse, O, L, bound, f"amax 448 causal={causal}"))
         # zero query rows: uniform weights, so O is the mean of the visible V rows
         v = e4m3_decode(v8) * vs
@@ -130,7 +144,7 @@ def test_fp8_per_head_descales_every_element(causal):
     (q8, qh), (k8, kh), (v8, vh) = (quantise_e4m3_per_head(t.float() * mag) for t in (q, k, v))
     scale = 1 / math.sqrt(d)
     O, L = attention_fp8_reference(q8, k8, v8, qh.numpy(), kh.numpy(), vh.numpy(), scale, causal)
-    bound = fp8_output_bound(q8, k8, v8, qh.numpy(), kh.numpy(), vh.numpy(), scale, causal)
+    bound = bounds(q8, k8, v8, qh.numpy(), kh.numpy(), vh.numpy(), scale, causal)
     # head 1 reaches scores of std ~64: float32 accumulation moves small-|LSE| rows
     sb = fp8_score_error_bound(q8, k8, qh.numpy(), kh.numpy(), scale, causal)
     for tensor_f in ((1.0, 1.0, 1.0), (2.0, 0.5, 4.0)):
@@ -154,9 +168,7 @@ def test_fp8_long_causal_sampled():
     deq = [torch.from_numpy(e4m3_decode(t) * s) for t, s in ((q8, qs), (k8, ks), (v8, vs))]
     for b, h in [(0, 0), (0, 9)]:
         O, L = oracle_rows(deq[0], deq[1], deq[2], scale, True, [(b, h)], rows)
-        bound = np.stack([fp8_output_bound(q8[b:b + 1, h:h + 1, i:i + 1], k8[b:b + 1, h:h + 1, :i + 1],
-                                           v8[b:b + 1, h:h + 1, :i + 1], qs, ks, vs, scale, False)[0, 0, 0]
-                          for i in rows])
+        bound = row_bounds(q8, k8, v8, qs, ks, vs, scale, b, h, rows)
         say(check(o[b, h, rows], lse[b, h, rows], O[0], L[0], bound, f"head {h}"))
 
 
@@ -180,9 +192,7 @@ def test_fp8_error_does_not_drift_with_sequence_length():
         errs, errs_in = [], []
         for h in (0, 1):
             O, L = oracle_rows(deq[0], deq[1], deq[2], scale, True, [(0, h)], rows)
-            bound = np.stack([fp8_output_bound(q8[:, h:h + 1, i:i + 1], k8[:, h:h + 1, :i + 1],
-                                               v8[:, h:h + 1, :i + 1], qs, ks, vs, scale, False)[0, 0, 0]
-                              for i in rows])
+            bound = row_bounds(q8, k8, v8, qs, ks, vs, scale, 0, h, rows)
             check(o[0, h, rows], lse[0, h, rows], O[0], L[0], bound, f"S={S} head {h}")
             errs.append(np.abs(o[0, h, rows] - O[0]))
             Ob, _ = oracle_rows(q, k, v, scale, True, [(0, h)], rows)
@@ -209,19 +219,26 @@ def test_fp8_longest_head_sampled():
     scale = 1 / math.sqrt(d)
     rows = [0, 131, 255, 256, 299]
     qq = dequantise(q8[:, :, rows], qs)
-    O_c, L_c, A_c, smax, vabs = [], [], [], -np.inf, 0.0
+    O_c, L_c, A_c, smax, vabs, sabs, qkabs = [], [], [], -np.inf, 0.0, 0.0, 0.0
     for a in range(0, Sk, 1 << 20):
         kk, vv = dequantise(k8[:, :, a:a + (1 << 20)], ks), dequantise(v8[:, :, a:a + (1 << 20)], vs)
         n = kk.shape[2]
         Oc, Lc = attention_partial(qq, kk, vv, scale, 0, 0, n)
         Ac, _ = attention_partial(qq, kk, np.abs(vv), scale, 0, 0, n)
         O_c.append(Oc); L_c.append(Lc); A_c.append(Ac)
-        smax = np.maximum(smax, scale * np.einsum("bhic,bhjc->bhij", qq, kk).max(axis=-1))
+        sc = scale * np.einsum("bhic,bhjc->bhij", qq, kk)
+        smax = np.maximum(smax, sc.max(axis=-1))
+        sabs = np.maximum(sabs, np.abs(sc).max(axis=-1))
+        qkabs = np.maximum(qkabs, np.einsum("bhic,bhjc->bhij", np.abs(qq), np.abs(kk)).max(axis=-1))
         vabs = vabs + np.abs(vv).sum(axis=2)
     O, L = merge_partials(np.stack(O_c), np.stack(L_c))
     A, _ = merge_partials(np.stack(A_c), np.stack(L_c))
     lmax = np.exp(L - smax)
-    bound = 2.0 ** -4 * A + 2.0 ** -10 * vabs[:, :, None, :] / lmax[..., None]
+    # fp8_output_bound and fp8_float32_bound from the same chunks
+    u = 2.0 ** -24
+    eps = d * u / (1 - d * u) * scale * qkabs + 8 * u * sabs
+    f32 = (np.expm1(2 * eps) + 2 * summation_gamma(Sk) + 16 * u)[..., None] * A
+    bound = 2.0 ** -4 * A + 2.0 ** -10 * vabs[:, :, None, :] / lmax[..., None] + f32
     say(check(o[:, :, rows], lse[:, :, rows], O, L, bound, "fp8 longest head"))
 
 

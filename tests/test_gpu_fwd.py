@@ -66,14 +66,23 @@ def test_config1_tiny_full():
     check_forward(o, lse, O, L, w.name)
 
 
-def _sampled(w, bh_list, rows, emu=0.0, tau=8.0):
+def _sampled(w, bh_list, rows, emu=0.0, tau=8.0, whole=None):
+    """The whole workload on the GPU, in the benchmark's launch configuration;
+    sampled rows of the heads in bh_list against the oracle, and every element
+    of the head `whole` (b, h)."""
     q, k, v = workload_inputs(w)
     o, lse = run_fwd(q, k, v, w.causal, tau=tau, emu=emu)
     O, L = oracle_rows(q, k, v, w.scale, w.causal, bh_list, rows)
     og = torch.stack([o[b, h, rows] for b, h in bh_list])
     lg = torch.stack([lse[b, h, rows] for b, h in bh_list])
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    return check_forward(og, lg, O, L, f"{w.name} emu={emu} tau={tau}")
+    st = check_forward(og, lg, O, L, f"{w.name} emu={emu} tau={tau}")
+    if whole is not None:
+        b, h = whole
+        Oh, Lh = attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.scale, w.causal)
+        st["whole_head"] = check_forward(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], Oh, Lh,
+                                         f"{w.name} head {whole} emu={emu} tau={tau}")
+    return st
 
 
 def _rows(S, n, seed):
@@ -86,7 +95,7 @@ def _rows(S, n, seed):
 def test_config2_sampled():
     w = WORKLOADS[2]
     say(f"fwd {w.name}")
-    st = _sampled(w, [(0, 0), (0, 7), (1, 15)], _rows(w.Sq, 48, 2))
+    st = _sampled(w, [(0, 0), (0, 7), (1, 15)], _rows(w.Sq, 48, 2), whole=(1, 15))
     say(st)
 
 
@@ -96,14 +105,14 @@ def test_extra_noncausal_long_sampled():
     from workloads import EXTRA_WORKLOADS
     w = EXTRA_WORKLOADS[6]
     say(f"fwd {w.name}")
-    st = _sampled(w, [(0, 0), (0, 11)], _rows(w.Sq, 32, 6))
+    st = _sampled(w, [(0, 0), (0, 11)], _rows(w.Sq, 32, 6), whole=(0, 5))
     say(st)
 
 
 def test_config3_causal_long_sampled():
     w = WORKLOADS[3]
     say(f"fwd {w.name}")
-    st = _sampled(w, [(0, 0), (0, 9)], _rows(w.Sq, 40, 3))
+    st = _sampled(w, [(0, 0), (0, 9)], _rows(w.Sq, 40, 3), whole=(0, 15))
     say(st)
 
 
@@ -111,8 +120,31 @@ def test_config3_causal_long_sampled():
 def test_config4_rescale_stress_sampled(emu):
     w = WORKLOADS[4]
     say(f"fwd {w.name} emu={emu}")
-    st = _sampled(w, [(0, 0), (3, 31)], _rows(w.Sq, 40, 4), emu=emu)
+    st = _sampled(w, [(0, 0), (3, 31)], _rows(w.Sq, 40, 4), emu=emu, whole=(3, 31))
     say(st)
+
+
+# The three launch forms of the forward: causal with enough 256-row blocks
+# for two per CU (256-row workgroups), causal with fewer (split 128-row
+# workgroups), and non-causal (256-row workgroups); S = 1000 leaves a ragged
+# last tile.  Causal inputs carry the rescale-stress key ramp.
+FORMS = {"causal-256row": (128, True, 6.0), "causal-split": (4, True, 6.0), "noncausal": (8, False, 0.0)}
+
+
+@pytest.mark.parametrize("emu", [0.1, 0.25, 0.5, 1.0])
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("d", [64, 128])
+def test_emulated_share_every_form_every_element(d, form, emu):
+    """Every software-exponential instantiation (shares 3, 8, 16 and 32 of 32)
+    in every launch form at both head dims, every element against the oracle
+    (FA4 §3.1.3, Table 2: the emulated share is exact up to rounding)."""
+    H, causal, ramp = FORMS[form]
+    S = 1000
+    say(f"fwd emu={emu} ({fa.fa_fwd_realised_emu_frac(d, emu):.4f} realised) d={d} {form} B1 H{H} S{S}")
+    q, k, v = make_inputs(1, H, S, S, d, seed=500 + d + H + int(emu * 100), key_ramp=ramp)
+    o, lse = run_fwd(q, k, v, causal, emu=emu)
+    O, L = attention_forward(q, k, v, 1 / math.sqrt(d), causal)
+    say(check_forward(o, lse, O, L, f"emu={emu} d={d} {form}"))
 
 
 @pytest.mark.parametrize("tau", [0.0, 8.0, 64.0])

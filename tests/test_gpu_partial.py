@@ -54,6 +54,25 @@ def test_partial_every_element(d, Sq, Sk, q_off, kb, ke, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tau,emu", [(0.0, 0.25), (64.0, 0.25), (0.0, 1.0), (64.0, 1.0), (8.0, 0.5)])
+@pytest.mark.parametrize("Sq,Sk,q_off,kb,ke,causal", [
+    (300, 1024, 0, 37, 900, False), (300, 1024, 500, 200, 1024, True), (1000, 1000, 0, 0, 1000, True),
+])
+def test_partial_tau_and_emulation_every_element(d, tau, emu, Sq, Sk, q_off, kb, ke, causal):
+    """The key-range forward at tau 0 (eager rescale), 64 (almost never) and
+    8, with software exponentials on a quarter, half or all of the scores;
+    keys carry the rescale-stress ramp so row maxima keep rising."""
+    say(f"partial d={d} tau={tau} emu={emu} Sq={Sq} Sk={Sk} q_off={q_off} keys {kb}..{ke} causal={causal}")
+    q, _, _ = make_inputs(1, 4, Sq, Sq, d, seed=Sq + d + 7)
+    _, k, v = make_inputs(1, 4, Sk, Sk, d, seed=Sk + d + 9, key_ramp=6.0)
+    o, lse = fa.forward_partial(q.to(DEV), k.to(DEV), v.to(DEV), q_off, kb, ke, causal=causal, tau=tau,
+                                emu_frac=emu)
+    torch.cuda.synchronize()
+    O, L = attention_partial(q, k, v, 1 / math.sqrt(d), q_off, kb, ke, causal)
+    say(check_partial(o.cpu(), lse.cpu(), O, L, f"d{d} tau={tau} emu={emu} {Sq}x{Sk} q_off={q_off} {kb}..{ke}"))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("n", [1, 3, 5])
 def test_merge_every_element(d, n):
     """Seeded synthetic parts (including empty rows in some parts and rows

@@ -98,3 +98,53 @@ def test_score_bound_holds_for_float32_sums():
             assert np.all(err <= bound)
         err_seq = np.where(vis, np.abs(seq.astype(np.float64) - exact), 0.0).max(axis=-1)
         assert np.max(err_seq / bound) > 5e-3     # 1.4e-2 here: a worst-case bound
+
+
+def test_summation_bound_holds_for_float32_sums():
+    """summation_gamma(n - 1) * sum |x| bounds the error of float32 sums of n
+    terms -- sequential (cumsum), pairwise (numpy) and torch's reduction --
+    of positive and of signed terms up to 4 M of them; the sequential sums of
+    positive terms reach a few percent of it (it is not vacuous)."""
+    from oracle import summation_gamma
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for n in (2, 100, 1000, 10_000, 1 << 20, 1 << 22):
+        for kind in ("pos", "signed"):
+            x = (rng.random(n) if kind == "pos" else rng.standard_normal(n)).astype(np.float32)
+            exact = float(np.sum(x.astype(np.float64)))
+            bound = float(summation_gamma(n - 1)) * float(np.sum(np.abs(x.astype(np.float64))))
+            sums = (np.cumsum(x, dtype=np.float32)[-1], np.sum(x, dtype=np.float32), torch.from_numpy(x).sum().item())
+            for s in sums:
+                assert abs(float(s) - exact) <= bound, (n, kind)
+            if kind == "pos" and n >= 1000:
+                worst = max(worst, abs(float(sums[0]) - exact) / bound)
+    assert worst > 0.02, worst
+
+
+def test_float32_pipeline_within_both_bounds():
+    """A float32 rendering of the e4m3 forward's arithmetic (scores summed in
+    float32, P = 2^(s c - m) in float32 rounded to e4m3 for P V, float32 row
+    sum and P V sums, one division) differs from exact attention of the
+    dequantised inputs by no more than fp8_output_bound + fp8_float32_bound."""
+    from oracle import fp8_float32_bound
+    g = torch.Generator().manual_seed(17)
+    B, H, S, d = 1, 2, 130, 64
+    q8, qs = _quantise(torch.randn(B, H, S, d, generator=g) * 3)
+    k8, ks = _quantise(torch.randn(B, H, S, d, generator=g) * 3)
+    v8, vs = _quantise(torch.randn(B, H, S, d, generator=g))
+    scale = 1 / math.sqrt(d)
+    q, k, v = (torch.from_numpy(dequantise(t, f)).float() for t, f in ((q8, qs), (k8, ks), (v8, vs)))
+    for causal in (False, True):
+        O, _ = attention_forward(q.double(), k.double(), v.double(), scale, causal)
+        s = (q @ k.transpose(-1, -2)) * torch.tensor(scale * 1.4426950408889634, dtype=torch.float32)
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), float("-inf"))
+        m = s.amax(dim=-1, keepdim=True)
+        p = torch.exp2(s - m)
+        p8 = p.to(torch.float8_e4m3fn).to(torch.float32)
+        o = (p8 @ v) / p.sum(dim=-1, keepdim=True)
+        err = np.abs(o.double().numpy() - O)
+        allowed = (fp8_output_bound(q8, k8, v8, qs, ks, vs, scale, causal)
+                   + fp8_float32_bound(q8, k8, v8, qs, ks, vs, scale, causal))
+        assert np.all(err <= allowed)
+        assert err.max() > 0.05 * allowed.max()
