@@ -16,12 +16,13 @@ import os
 __all__ = [
     "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
     "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
-    "backward", "LIB_PATH",
+    "backward", "fa_bwd_noalloc", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
+FA_NOALLOC_MAX_ROWS = 1 << 21
 FA_BWD_PREPARE, FA_BWD_DQ, FA_BWD_DKDV, FA_BWD_ALL = 1, 2, 4, 7
 
 _lib = None
@@ -59,6 +60,8 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = sz
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_bwd.restype = i
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.fa_bwd_noalloc.restype = i
     L.fa_bwd_phase.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_bwd_phase.restype = i
     L.fa_exp2_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
@@ -249,6 +252,25 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=Non
                       _ptr(workspace), ws_bytes, _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None, deterministic=False):
+    """fa_bwd without a caller workspace (the library's fixed scratch; no
+    device allocation): fills dq, dk, dv in place."""
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    for name, t, s in (("q", q, (B, H, Sq, d)), ("k", k, (B, H, Sk, d)), ("v", v, (B, H, Sk, d)),
+                       ("o", o, (B, H, Sq, d)), ("dout", dout, (B, H, Sq, d)), ("dq", dq, (B, H, Sq, d)),
+                       ("dk", dk, (B, H, Sk, d)), ("dv", dv, (B, H, Sk, d))):
+        _check_bf16(name, t, s)
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, Sq, Sk, d, int(bool(causal)), float(scale), int(bool(deterministic)),
+                              _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc")
 
 
 def fa_exp2_probe(x, y_hw, y_emu):

@@ -38,6 +38,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_INVALID: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_SCRATCH: return "request exceeds the library's fixed scratch (B * H * Sq > FA_NOALLOC_MAX_ROWS)";
   }
   return "unknown status";
 }
@@ -214,6 +215,36 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_bwd_phase(FA_BWD_ALL, Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Sq, Sk, d, causal, scale, deterministic,
                       workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                         const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d,
+                         int causal, float scale, int deterministic, void* stream) {
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_INVALID;
+  const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (deterministic != 0 && deterministic != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+  if (fa::bwd_workspace_bytes(B, H, Sq, Sk, d, deterministic != 0) > fa::kScratchBytes) return FA_ERR_SCRATCH;
+
+  void* ws = nullptr;
+  if (fa::bwd_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  fa::BwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE; a.dout = dO;
+  a.dq = dQ; a.dk = dK; a.dv = dV;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.deterministic = deterministic != 0;
+  a.workspace = ws;
+  const hipError_t e = fa::launch_bwd(a, fa::kBwdPrepare | fa::kBwdDq | fa::kBwdDkdv, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status fa_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, void* stream) {

@@ -25,6 +25,7 @@
 // fa_tiles.hpp, so Q, dO, K and V are each read both row-wise and transposed
 // from one LDS copy.
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -718,6 +719,36 @@ hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t 
 }
 
 }  // namespace
+
+// ------------------------------------------------- fixed scratch
+// Scratch of the allocation-free backward: the row terms (D and LSE log2 e,
+// the workspace of launch_bwd) of up to kScratchRows query rows, in a
+// file-scope device array.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, and is kept here.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t bwd_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int /*d*/, bool /*deterministic*/) {
   return 2 * ((((size_t)B * H * Sq * sizeof(float)) + 255) & ~size_t(255));

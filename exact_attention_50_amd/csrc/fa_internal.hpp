@@ -70,6 +70,11 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int B, int H, int Sq, int Sk, int d, bool deterministic);
+// Fixed device scratch for the allocation-free backward: 16 MiB holds the
+// workspace of B * H * Sq <= 2^21 query rows (two 8 MiB sections).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+// This device's scratch address (resolved once per device; no allocation).
+hipError_t bwd_scratch(void** out);
 // phases: bit mask of the kernels to enqueue, in this order
 constexpr int kBwdPrepare = 1, kBwdDq = 2, kBwdDkdv = 4;
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);

@@ -46,7 +46,8 @@ typedef enum {
   FA_ERR_INVALID = 1,      /* null pointer, bad size, bad scalar, misaligned pointer, small workspace */
   FA_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement (d, causal Sq != Sk,
                               a head longer than the limit below) */
-  FA_ERR_HIP = 3           /* the HIP runtime reported an error while launching */
+  FA_ERR_HIP = 3,          /* the HIP runtime reported an error while launching */
+  FA_ERR_SCRATCH = 4       /* a no-allocation entry point was asked for more than its fixed scratch holds */
 } fa_status;
 
 /* Head dimensions the kernels are built for.  One head of any tensor must
@@ -197,6 +198,29 @@ fa_status fa_bwd_phase(int phases, const void* Q, const void* K, const void* V, 
                        const void* dO, void* dQ, void* dK, void* dV,
                        int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results as fa_bwd (bit for bit), with the workspace taken
+ * from a fixed scratch array inside the library instead of a caller buffer.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); on its first call on a device it looks up that device's copy of
+ * the array (16 MiB per GPU, held until the process ends).
+ *   Limit: B * H * Sq <= FA_NOALLOC_MAX_ROWS (2^21); larger requests return
+ *   FA_ERR_SCRATCH before anything is enqueued.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *   one GPU (different streams, or host threads without ordering) race and
+ *   give wrong gradients.  Calls on one stream are ordered and safe.  The
+ *   scratch keeps the last call's contents; nothing in it needs clearing
+ *   (every row term is written before it is read).
+ *   Other arguments, validation and errors as for fa_bwd.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_SCRATCH or
+ * FA_ERR_HIP. */
+#define FA_NOALLOC_MAX_ROWS (1 << 21)
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                         const void* dO, void* dQ, void* dK, void* dV,
+                         int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
+                         void* stream);
 
 /* Element-wise probe of the two exponentials the forward uses, so their
  * agreement can be measured (paper §3.1.3, Table 2): y_hw[i] = hardware

@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(4):
-        assert fa.fa_status_str(s)
+    for s in range(5):
+        assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
 
 
@@ -160,3 +160,29 @@ def test_bwd_phase_mask_validation(L):
     bad = list(args)
     bad[13] = 96   # d
     assert L.fa_bwd_phase(fa.FA_BWD_DQ, *bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_noalloc_validation(L):
+    """The allocation-free backward validates like fa_bwd and refuses requests
+    beyond its fixed scratch (B * H * Sq > FA_NOALLOC_MAX_ROWS) before any
+    HIP call."""
+    vp = ctypes.c_void_p
+
+    def call(B=1, H=2, Sq=100, Sk=100, d=64, causal=1, scale=0.125, det=1, null=None, mis=None):
+        ptrs = [FAKE] * 9
+        if null is not None:
+            ptrs[null] = 0
+        if mis is not None:
+            ptrs[mis] = FAKE + 8
+        return L.fa_bwd_noalloc(*[vp(p) for p in ptrs], B, H, Sq, Sk, d, causal, scale, det, vp(0))
+    assert call(null=0) == fa.FA_ERR_INVALID
+    assert call(null=8) == fa.FA_ERR_INVALID
+    assert call(mis=4) == fa.FA_ERR_INVALID
+    assert call(scale=0.0) == fa.FA_ERR_INVALID
+    assert call(det=2) == fa.FA_ERR_INVALID
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(Sk=50) == fa.FA_ERR_UNSUPPORTED          # causal, Sq != Sk
+    limit = fa.FA_NOALLOC_MAX_ROWS
+    assert call(B=2, H=16, Sq=limit // 32 + 1, Sk=limit // 32 + 1) == fa.FA_ERR_SCRATCH
+    assert call(B=1, H=1, Sq=limit + 1, Sk=limit + 1, causal=0) == fa.FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_status_str(fa.FA_ERR_SCRATCH)
