@@ -98,6 +98,16 @@ __device__ __forceinline__ float exp2_sw(float x) {
   return x < -126.0f ? 0.0f : r;
 }
 
+// ---------------------------------------------------------------------------
+// The online softmax of one key tile, shared by the bf16 and e4m3 forwards
+// (FlashAttention-4 paper §3.1.4, Eq. 6, as summarised on "FlashAttention-4:
+// Algorithm and Kernel Pipelining Co-Design for Asymmetric Hardware
+// Scaling").  A wavefront holds S^T of KB 32-key blocks in the MFMA C layout:
+// lane (r, g) holds 16 scores of query r per block, element i of block kb
+// being key 32 kb + 8 (i / 4) + 4 g + i % 4 of the tile.  The kernels call
+// these steps in order: mask (edge tiles only), row max, conditional
+// rescale, exponentials with row sums; then each packs P for its products.
+
 // x if C <= lim, else -inf: one compare into VCC and one select, so that a
 // run of these keeps no lane masks alive in scalar registers.
 template <int C>
@@ -109,6 +119,45 @@ __device__ __forceinline__ float keep_if_le(float x, int lim) {
       : "vcc");
   return r;
 }
+
+// Causal / ragged-end mask: the keys a row sees form a prefix of the tile,
+// so score (kb, i) is kept iff 32 kb + 8 (i / 4) + i % 4 <= lim, where lim is
+// (the row's last visible key) - (tile's first key) - 4 g; masked scores
+// become -inf (so their P is exactly 0).
+template <int KB>
+__device__ __forceinline__ void softmax_mask_prefix(f32x16 (&s)[KB], int lim);
+
+// The row max of the raw scores over the lane pair (l, l ^ 32): 8 independent
+// chains of v_max3_f32 (two scores per instruction), then a short tree.
+template <int KB>
+__device__ __forceinline__ float softmax_row_max(const f32x16 (&s)[KB]);
+
+// The conditional rescale: m_new = max(m_ref, m_tile) (log2 units); if any
+// row of the wavefront rose by more than tau over its reference (a
+// wave-uniform branch, "gated at warp granularity"), rescale(alpha) applies
+// alpha = 2^(m_ref - m_new) to this lane's running output and sums, where
+// only the rows that rose by more than tau move their reference (the others
+// get alpha = 1 exactly).  The first tile (m_ref = -inf) always takes it.
+// Returns whether the branch was taken.
+template <typename Rescale>
+__device__ __forceinline__ bool softmax_conditional_rescale(float& m_ref, float m_tile, float tau,
+                                                            Rescale&& rescale) {
+  const float m_new = __builtin_fmaxf(m_ref, m_tile);
+  const bool need = (m_new - m_ref) > tau;   // first tile: +inf > tau
+  if (__any(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;   // 2^-inf = 0
+    rescale(alpha);
+    m_ref = need ? m_new : m_ref;
+    return true;
+  }
+  return false;
+}
+
+// P = 2^(s c - m_ref) for every score (c: the score scale in log2 units) and
+// the four partial row sums of this lane; the first EMU of every 32 scores of
+// a lane (per 64 keys) use the software 2^x, the others v_exp_f32.
+template <int KB, int EMU>
+__device__ __forceinline__ void softmax_exp_rowsum(f32x16 (&s)[KB], float c, float m_ref, float (&l_part)[4]);
 
 // Exchange a value with the other half of the wave (lane l <-> l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
@@ -239,4 +288,47 @@ __device__ __forceinline__ int quad_slot(int quad_in_group) {
   return ((quad_in_group & 1) << 1) | ((quad_in_group >> 1) & 1);
 }
 
+template <int KB>
+__device__ __forceinline__ void softmax_mask_prefix(f32x16 (&s)[KB], int lim) {
+  static_for<KB * 16>([&](auto e) __attribute__((always_inline)) {
+    constexpr int kb = decltype(e)::value / 16, i = decltype(e)::value % 16;
+    s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
+  });
+}
+
+template <int KB>
+__device__ __forceinline__ float softmax_row_max(const f32x16 (&s)[KB]) {
+  constexpr int kPerChain = KB * 16 / 8;
+  auto score = [&](int e) __attribute__((always_inline)) -> float { return s[e / 16][e % 16]; };
+  float m8[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    m8[c] = score(c);
+#pragma unroll
+    for (int k = 1; k + 1 < kPerChain; k += 2) m8[c] = max3(m8[c], score(c + 8 * k), score(c + 8 * (k + 1)));
+    // (max3 with a repeated operand, so no fmaxf has to canonicalise an asm result)
+    if constexpr (kPerChain % 2 == 0) {
+      const float x = score(c + 8 * (kPerChain - 1));
+      m8[c] = max3(m8[c], x, x);
+    }
+  }
+  const float mx = max3(max3(m8[0], m8[1], m8[2]), max3(m8[3], m8[4], m8[5]), max3(m8[6], m8[7], m8[7]));
+  return pair_max(mx);
+}
+
+template <int KB, int EMU>
+__device__ __forceinline__ void softmax_exp_rowsum(f32x16 (&s)[KB], float c, float m_ref, float (&l_part)[4]) {
+  const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;   // no key yet: every P is 2^-inf = 0
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = __builtin_fmaf(s[kb][i], c, neg_m);
+      const float e = ((kb & 1) * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
+      s[kb][i] = e;
+      l_part[i & 3] += e;
+    }
+}
+
 }  // namespace fa
+

@@ -272,41 +272,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int k0 = tile_of(t) * kBN;
     const bool need_mask = (k0 + kBN > p.k_len) || (CAUSAL && k0 + kBN - 1 > q_diag + q_wave_lo);
     if (need_mask) {
-      // the keys a row sees form a prefix of the tile: score (kb, i) of this
-      // lane is key k0 + 32 kb + 8 (i / 4) + 4 g + i % 4, kept iff that key
-      // is below k_len (and, causal, at most the row's diagonal)
+      // key (kb, i) of this lane is k0 + 32 kb + 8 (i / 4) + 4 g + i % 4; it
+      // is kept iff below k_len (and, causal, at most the row's diagonal)
       const int last = CAUSAL ? min(p.k_len - 1, q_diag + q_lane) : p.k_len - 1;
-      const int lim = last - k0 - 4 * g;
-      static_for<kKB * 16>([&](auto e) __attribute__((always_inline)) {
-        constexpr int kb = decltype(e)::value / 16, i = decltype(e)::value % 16;
-        s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
-      });
+      softmax_mask_prefix<kKB>(s, last - k0 - 4 * g);
     }
-    // row max: 8 independent chains of v_max3_f32 (two scores per
-    // instruction), then a short tree
-    constexpr int kPerChain = kKB * 16 / 8;
-    auto score = [&](int e) __attribute__((always_inline)) -> float { return s[e / 16][e % 16]; };
-    float m8[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      m8[c] = score(c);
-#pragma unroll
-      for (int k = 1; k + 1 < kPerChain; k += 2) m8[c] = max3(m8[c], score(c + 8 * k), score(c + 8 * (k + 1)));
-      // (max3 with a repeated operand, so no fmaxf has to canonicalise an asm result)
-      if constexpr (kPerChain % 2 == 0) {
-        const float x = score(c + 8 * (kPerChain - 1));
-        m8[c] = max3(m8[c], x, x);
-      }
-    }
-    float mx = max3(max3(m8[0], m8[1], m8[2]), max3(m8[3], m8[4], m8[5]), max3(m8[6], m8[7], m8[7]));
-    mx = pair_max(mx);
-    const float m_new = __builtin_fmaxf(m_ref, mx * p.scale_log2);
-    // conditional rescale: wave-uniform branch; only rows whose max rose by
-    // more than tau move their reference, the others multiply by exactly 1
-    const bool need = (m_new - m_ref) > p.tau;   // first tile: +inf > tau
-    if (__any(need)) {
-      if constexpr (COUNT) n_events += t > 0 ? 1 : 0;
-      const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;   // exp2(-inf) = 0
+    const float mx = softmax_row_max<kKB>(s);
+    const bool corrected = softmax_conditional_rescale(m_ref, mx * p.scale_log2, p.tau, [&](float alpha) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
       // the selector sums hold queries lane % 16 and lane % 16 + 16
@@ -314,18 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       lh4[1] *= __shfl(alpha, (lane & 15) + 16);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
-      m_ref = need ? m_new : m_ref;
-    }
-    const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = __builtin_fmaf(s[kb][i], p.scale_log2, neg_m);
-        const float e = ((kb & 1) * 16 + i < EMU) ? exp2_sw(x) : exp2_hw(x);
-        s[kb][i] = e;
-        l_part[i & 3] += e;
-      }
+    });
+    if constexpr (COUNT) n_events += (corrected && t > 0) ? 1 : 0;
+    (void)corrected;
+    softmax_exp_rowsum<kKB, EMU>(s, p.scale_log2, m_ref, l_part);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       const int kb = ks >> 1, h = (ks & 1) * 8;
@@ -426,10 +390,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     // vector(t) = softmax of S_t.  A causal wave has nothing to do after tile
     // n_wave - 1 but keeps taking part in the barriers and the loads.  Every
     // wave issues its share of fetch(u) in interval 2u-1 and commits at the
-    // end of every even interval.  Each variant of the matrix phase appears
-    // in a straight-line position of its own so the accumulators are never
-    // merged across branches.  Prologue: K_0 is loaded and readable in
-    // interval 1.
+    // end of every even interval.  Each variant of the matrix phase has one
+    // call site (the last P V is matrix_pv(n_wave), n_wave = n when the wave
+    // has no tile left), so the compiler never merges two copies of a phase
+    // at a branch join (which cost registers and copies).  Prologue: K_0 is
+    // loaded and readable in interval 1.
     fetch(0);
     commit(0);
     barrier();
@@ -448,10 +413,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         commit(0);
         barrier();
       }
+      // one call site of the last P V (n_wave = n when nothing is left)
+      if (n_wave < n) fetch(n_wave + 1);
+      matrix_pv(n_wave);
+      barrier();
       if (n_wave < n) {
-        fetch(n_wave + 1);
-        matrix_pv(n_wave);
-        barrier();
         commit(0);
         barrier();
         for (int t = n_wave + 1; t < n; ++t) {
@@ -461,12 +427,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           barrier();
         }
         barrier();
-        barrier();
-      } else {
-        matrix_pv(n);
-        barrier();
-        barrier();
       }
+      barrier();
     } else {
       fetch(1);
       barrier();
@@ -484,8 +446,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         vector(t);
         barrier();
       }
+      matrix_pv(n_wave);
       if (n_wave < n) {
-        matrix_pv(n_wave);
         commit(0);
         barrier();
         fetch(n_wave + 2);
@@ -496,11 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           fetch(t + 2);
           barrier();
         }
-        barrier();
-      } else {
-        matrix_pv(n);
-        barrier();
       }
+      barrier();
     }
   }
   if constexpr (COUNT) {

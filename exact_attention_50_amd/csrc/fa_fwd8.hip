@@ -267,46 +267,16 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     const bool need_mask = (k0 + kBN8 > p.Sk) || (CAUSAL && k0 + kBN8 - 1 > q_wave_lo);
     if (need_mask) {
       const int last = CAUSAL ? min(p.Sk - 1, q_lane) : p.Sk - 1;
-      const int lim = last - k0 - 4 * g;
-      static_for<kKB * 16>([&](auto e) __attribute__((always_inline)) {
-        constexpr int kb = decltype(e)::value / 16, i = decltype(e)::value % 16;
-        s[kb][i] = keep_if_le<kb * 32 + 8 * (i >> 2) + (i & 3)>(s[kb][i], lim);
-      });
+      softmax_mask_prefix<kKB>(s, last - k0 - 4 * g);
     }
-    constexpr int kPerChain = kKB * 16 / 8;
-    auto score = [&](int e) __attribute__((always_inline)) -> float { return s[e / 16][e % 16]; };
-    float m8c[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      m8c[c] = score(c);
-#pragma unroll
-      for (int k = 1; k + 1 < kPerChain; k += 2) m8c[c] = max3(m8c[c], score(c + 8 * k), score(c + 8 * (k + 1)));
-      if constexpr (kPerChain % 2 == 0) {
-        const float x = score(c + 8 * (kPerChain - 1));
-        m8c[c] = max3(m8c[c], x, x);
-      }
-    }
-    float mx = max3(max3(m8c[0], m8c[1], m8c[2]), max3(m8c[3], m8c[4], m8c[5]), max3(m8c[6], m8c[7], m8c[7]));
-    mx = pair_max(mx);
-    const float m_new = __builtin_fmaxf(m_ref, mx * s_log2);
-    const bool need = (m_new - m_ref) > p.tau;
-    if (__any(need)) {
-      const float alpha = need ? exp2_hw(m_ref - m_new) : 1.0f;
+    const float mx = softmax_row_max<kKB>(s);
+    softmax_conditional_rescale(m_ref, mx * s_log2, p.tau, [&](float alpha) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
-      m_ref = need ? m_new : m_ref;
-    }
-    const float neg_m = (m_ref == kNegInf) ? 0.0f : -m_ref;
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = exp2_hw(__builtin_fmaf(s[kb][i], s_log2, neg_m));
-        s[kb][i] = e;
-        l_part[i & 3] += e;
-      }
+    });
+    softmax_exp_rowsum<kKB, 0>(s, s_log2, m_ref, l_part);
     // P^T operand of 64-key step ks: bytes j = 0..31 are s[2 ks + j / 16][j % 16]
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)

@@ -3,31 +3,50 @@
 Method followed: the FA4 paper summary ("FlashAttention-4: Algorithm and
 Kernel Pipelining Co-Design for Asymmetric Hardware Scaling"), Key claims:
 per-tile roofline of §3.1.1 / Table 1 (forward) and §3.2.1 / Eq. 7-8
-(backward).  The kernel's time per tile is bounded by the busiest of three
-units: the matrix unit, the exponential unit and on-chip operand memory.
+(backward).  A tile's time is bounded by the busiest unit: the matrix unit,
+the exponential unit and on-chip operand memory (and, on CDNA4, the vector
+ALU's issue, which the exponentials share).
 
-Hardware constants.  B200 per SM, as the pages state them: matrix unit 8192
-dense bf16 FLOP per clock (the divisor in Eq. 7), exponential unit 16 per
-clock, shared-memory reads 128 bytes per clock.  MI355X (gfx950) per CU, from
-AMD's public figures: 4096 dense bf16 FLOP per clock (2.5 PFLOP/s over 256
-CUs at 2.4 GHz); the transcendental rate and LDS bandwidth are parameters
-that the microbenchmarks measure.
+B200 per SM, as the pages state them: matrix unit 8192 dense bf16 FLOP per
+clock (the divisor in Eq. 7), exponential unit 16 per clock, shared-memory
+reads 128 bytes per clock.  Operand-memory reading (ours; it reproduces
+Table 1's printed 1536 cycles): each 128-row query tile of the 256-row tile
+issues Q K^T with both operands in shared memory and P V with V in shared
+memory, so one tile step reads (M/128) * (128 d + 2 N d) bf16 values.
 
-Operand-memory reading (ours; it reproduces Table 1's printed 1536 cycles):
-on B200 each 128-row query tile of the 256-row tile issues Q K^T with both
-operands in shared memory and P V with V in shared memory, so one tile step
-reads (M/128) * (128 d + 2 N d) bf16 values.  On CDNA4 Q stays in registers
-and every wavefront that owns ``rows_per_wave`` query rows reads the whole K
-and V tile from LDS: (M / rows_per_wave) * 2 N d bf16 values.
+MI355X (gfx950) per compute unit (4 SIMDs).  The matrix rate is AMD's
+published figure (2.5 PFLOP/s dense bf16 = 256 CUs x 2.4 GHz x 4096 FLOP per
+clock).  The other rates are measured on MI355X by
+exact_attention_50_amd/probes/unit_rates.hip (cycles per wavefront-of-64
+instruction on one SIMD, enough independent work to reach throughput):
+  * v_mfma_f32_32x32x16_bf16 32.1 cycles (4096 FLOP/clock/CU, as published),
+    v_mfma_f32_16x16x32_bf16 17.1 cycles;
+  * VALU fp32 (fma, add, max3, cvt_pk_bf16): 4.3 cycles per instruction per
+    SIMD when two wavefronts issue (one wavefront alone reaches ~6 and, with
+    only 8 independent chains, ~9.5: a dependent VALU instruction waits
+    ~40 cycles);
+  * v_exp_f32: 9.1 cycles per instruction per SIMD (two wavefronts; ~9.7 for
+    one) -- the exponential shares the VALU issue;
+  * LDS operand reads with 8 wavefronts per CU: ds_read_b128 213 bytes per
+    clock per CU, ds_read_b64_tr_b16 (transposed MFMA operands) 128 bytes
+    per clock per CU (half of each with 4 wavefronts: the reads are latency
+    bound below 8 wavefronts);
+  * an MFMA wavefront and a VALU wavefront sharing a SIMD both keep their own
+    rate (32.0 and 6.2 cycles), so matrix and vector work overlap.
+On CDNA4 Q stays in registers (the B operand of S^T = K Q^T); every
+wavefront of ``rows_per_wave`` query rows reads the whole K tile row-wise and
+the V tile transposed from LDS.
 """
 
 B200_SM = dict(name="B200 SM", mma_flops_per_clk=8192.0, exp_per_clk=16.0,
                smem_bytes_per_clk=128.0)
 
-# MI355X per compute unit.  exp and LDS rates are planning values until
-# measured; callers override them with measured numbers.
-MI355X_CU = dict(name="MI355X CU", mma_flops_per_clk=4096.0, exp_per_clk=16.0,
-                 smem_bytes_per_clk=128.0, clock_hz=2.4e9, n_cu=256)
+MI355X_CU = dict(name="MI355X CU", mma_flops_per_clk=4096.0, clock_hz=2.4e9, n_cu=256, simds=4,
+                 mfma16_cycles=17.1,          # v_mfma_f32_16x16x32_bf16, per SIMD
+                 valu_cycles=4.3,             # fp32 VALU instruction (wave64), per SIMD
+                 exp_cycles=9.1,              # v_exp_f32 (wave64), per SIMD
+                 lds_row_bytes_per_clk=213.0,     # ds_read_b128, per CU
+                 lds_tr_bytes_per_clk=128.0)      # ds_read_b64_tr_b16, per CU
 
 
 def forward_tile_cycles_b200(M, N, d, hw=B200_SM, qtile_rows=128, elem_bytes=2):
@@ -45,21 +64,59 @@ def backward_tile_mma_cycles(M, N, d, hw=B200_SM):
     return 10.0 * M * N * d / hw["mma_flops_per_clk"]
 
 
-def forward_tile_cycles_cdna4(M, N, d, rows_per_wave, hw=MI355X_CU,
-                              other_valu_per_score=3.0, valu_lanes_per_clk=64.0,
-                              elem_bytes=2):
-    """Per-CU cycles for one forward tile on CDNA4 (4 SIMDs share the CU).
+def _per_cu(n_instr, cycles_per_instr, hw):
+    """CU cycles for n_instr wave64 instructions spread over the CU's SIMDs."""
+    return n_instr * cycles_per_instr / hw["simds"]
 
-    other_valu_per_score: non-exp vector ops per score (scale-subtract FMA,
-    max, add, half a bf16 pack) at ``valu_lanes_per_clk`` lanes per clock per
-    CU (4 SIMDs x 16 lanes).
+
+def forward_tile_cycles_cdna4(M, N, d, rows_per_wave=32, valu_per_score=3.2, row_sum_mfma=True,
+                              hw=MI355X_CU, elem_bytes=2):
+    """CU cycles of each unit for one (M query rows) x (N keys) forward tile.
+
+    mma    the S^T and P V products, 4 M N d FLOPs, plus (row_sum_mfma) one
+           16x16x32 product per 32 rows and 16 keys that sums the bf16 weights;
+    exp    one v_exp_f32 per score (M N / 64 instructions);
+    valu   valu_per_score other VALU instructions per score (scale-subtract,
+           row max, row sum, half a bf16 pack: about 3.2 in the bf16 kernel);
+    issue  exp + valu: both go through the VALU issue of the SIMD;
+    lds    every wavefront reads the K tile row-wise and the V tile
+           transposed: (M / rows_per_wave) N d bytes of each.
     """
     mma = 4.0 * M * N * d / hw["mma_flops_per_clk"]
-    exp = 1.0 * M * N / hw["exp_per_clk"]
-    valu = other_valu_per_score * M * N / valu_lanes_per_clk
-    lds_bytes = (M / rows_per_wave) * 2 * N * d * elem_bytes
-    lds = lds_bytes / hw["smem_bytes_per_clk"]
-    return dict(mma=mma, exp=exp, valu=valu, lds=lds)
+    if row_sum_mfma:
+        mma += _per_cu((M / 32) * (N / 16), hw["mfma16_cycles"], hw)
+    exp = _per_cu(M * N / 64, hw["exp_cycles"], hw)
+    valu = _per_cu(valu_per_score * M * N / 64, hw["valu_cycles"], hw)
+    tile_bytes = (M / rows_per_wave) * N * d * elem_bytes
+    lds = tile_bytes / hw["lds_row_bytes_per_clk"] + tile_bytes / hw["lds_tr_bytes_per_clk"]
+    return dict(mma=mma, exp=exp, valu=valu, issue=exp + valu, lds=lds)
+
+
+def gradient_tile_cycles_cdna4(M_own, N_stream, d, products, row_reads, tr_reads, valu_per_elem=6.0,
+                               hw=MI355X_CU, elem_bytes=2):
+    """CU cycles of each unit for one tile of a gradient kernel: a workgroup
+    owning M_own rows (keys for dK/dV, queries for dQ) against N_stream
+    streamed rows, with ``products`` matrix products of 2 M N d FLOPs each
+    (4 for dK/dV: S, dP, dV, dK; 3 for dQ: S, dP, dQ), one exponential and
+    valu_per_elem other VALU instructions per (own, streamed) pair, and
+    row_reads / tr_reads streamed-tile reads per wavefront of 32 own rows
+    (row-wise and transposed: Q, dO / K, V read as each kind of operand)."""
+    mma = 2.0 * products * M_own * N_stream * d / hw["mma_flops_per_clk"]
+    exp = _per_cu(M_own * N_stream / 64, hw["exp_cycles"], hw)
+    valu = _per_cu(valu_per_elem * M_own * N_stream / 64, hw["valu_cycles"], hw)
+    tile_bytes = (M_own / 32) * N_stream * d * elem_bytes
+    lds = (row_reads * tile_bytes / hw["lds_row_bytes_per_clk"]
+           + tr_reads * tile_bytes / hw["lds_tr_bytes_per_clk"])
+    return dict(mma=mma, exp=exp, valu=valu, issue=exp + valu, lds=lds)
+
+
+def bound(cycles):
+    """The unit with the most cycles among mma, issue and lds (and its share
+    of the tile time for every unit: predicted busy fractions)."""
+    units = {k: cycles[k] for k in ("mma", "issue", "lds")}
+    name = max(units, key=units.get)
+    top = units[name]
+    return name, {k: v / top for k, v in units.items()}
 
 
 def peak_bf16_tflops(hw=MI355X_CU):

@@ -28,8 +28,58 @@ def test_mi355x_peak():
     assert abs(roofline.peak_bf16_tflops() - 2516.58) < 0.01
 
 
-def test_cdna4_tile_model_scales():
-    a = roofline.forward_tile_cycles_cdna4(256, 128, 128, rows_per_wave=32)
-    b = roofline.forward_tile_cycles_cdna4(256, 128, 128, rows_per_wave=64)
-    assert a["mma"] == 4096.0 and a["exp"] == 2048.0
-    assert a["lds"] == 2 * b["lds"]
+def _close(a, b):
+    return abs(a - b) <= 1e-9 * max(1.0, abs(b))
+
+
+def test_cdna4_forward_tile_terms_hand_derived():
+    """Each term of the CDNA4 forward tile model against values worked by
+    hand from the MI355X rates (the 256 x 128 tile of Table 1's shape):
+    d = 128: mma = 4*256*128*128/4096 = 4096 plus 8*8 16x16x32 row-sum
+    products of 17.1 cycles over 4 SIMDs = 273.6; exp = 512 v_exp_f32 x 9.1 / 4
+    = 1164.8; valu = 3.2 x 512 x 4.3 / 4 = 1761.28; LDS = 8 waves x 128 keys x
+    128 dims x 2 bytes = 262144 bytes read row-wise at 213 B/clk plus the same
+    transposed at 128 B/clk = 1230.7324 + 2048.  d = 64 halves the matrix
+    and LDS terms."""
+    c = roofline.forward_tile_cycles_cdna4(256, 128, 128)
+    assert _close(c["mma"], 4369.6)
+    assert _close(c["exp"], 1164.8)
+    assert _close(c["valu"], 1761.28)
+    assert _close(c["issue"], 2926.08)
+    assert _close(c["lds"], 262144 / 213 + 2048.0)
+    assert roofline.bound(c)[0] == "mma"
+    c64 = roofline.forward_tile_cycles_cdna4(256, 128, 64)
+    assert _close(c64["mma"], 2048 + 273.6)
+    assert _close(c64["lds"], 131072 / 213 + 1024.0)
+    assert _close(c64["issue"], 2926.08)
+    name, frac = roofline.bound(c64)
+    assert name == "issue" and _close(frac["mma"], 2321.6 / 2926.08)
+    # without the row-sum products the matrix term is the plain 4 M N d / 4096
+    assert roofline.forward_tile_cycles_cdna4(256, 128, 128, row_sum_mfma=False)["mma"] == 4096.0
+
+
+def test_cdna4_gradient_tile_terms_hand_derived():
+    """dK/dV tile: 128 keys x 64 streamed query rows, d = 128, four products
+    (S, dP, dV, dK): mma = 2*4*128*64*128/4096 = 2048; exp = 128 instructions
+    x 9.1 / 4 = 291.2; valu = 6 x 128 x 4.3 / 4 = 825.6; LDS: 4 waves x 64 rows
+    x 128 dims x 2 bytes = 65536 bytes, read twice row-wise (Q, dO) and twice
+    transposed (dO^T, Q^T) = 2*65536/213 + 2*65536/128.  dQ tile (three
+    products, two row-wise and one transposed read) = 1536 and
+    2*65536/213 + 65536/128."""
+    c = roofline.gradient_tile_cycles_cdna4(128, 64, 128, products=4, row_reads=2, tr_reads=2)
+    assert _close(c["mma"], 2048.0) and _close(c["exp"], 291.2) and _close(c["valu"], 825.6)
+    assert _close(c["lds"], 2 * 65536 / 213 + 1024.0)
+    assert roofline.bound(c)[0] == "mma"
+    q = roofline.gradient_tile_cycles_cdna4(128, 64, 128, products=3, row_reads=2, tr_reads=1)
+    assert _close(q["mma"], 1536.0) and _close(q["lds"], 2 * 65536 / 213 + 512.0)
+
+
+def test_cdna4_model_at_b200_rates_is_table1():
+    """The CDNA4 forward model with the B200 rates the page states (matrix
+    8192 FLOP/clock, 16 exponentials per clock on one unit, 128 bytes per
+    clock) and one wavefront per 128 rows reading K and V once each gives
+    Table 1's matrix and exponential cycles, 2048 and 2048: the two models
+    differ only in the unit rates and the operand reads."""
+    b200_like = dict(roofline.MI355X_CU, mma_flops_per_clk=8192.0, simds=1, exp_cycles=64 / 16.0)
+    c = roofline.forward_tile_cycles_cdna4(256, 128, 128, row_sum_mfma=False, hw=b200_like)
+    assert c["mma"] == 2048.0 and c["exp"] == 2048.0
