@@ -30,6 +30,9 @@ Modules
                    disjoint ranges -- the single-GPU pieces of ring attention.
   fp8              e4m3 decoding, exact attention of dequantised e4m3 inputs,
                    and the per-element error bound of rounding P to e4m3.
+  mxfp4            MXFP4 (E2M1 elements, E8M0 scales per 32) decoding and
+                   exact attention of MXFP4 Q, K with e4m3 V, with the bounds
+                   of ``fp8`` on the decoded tensors.
   roofline         per-tile cycle model (paper §3.1.1 Table 1; §3.2.1 Eq. 7-8)
                    with B200 constants and with CDNA4 constants.
 
@@ -47,6 +50,7 @@ from .exp2_emulation import (fit_exp2_minimax, exp2_emulated_f32, bf16_round,
 from .partial import attention_partial, merge_partials
 from .fp8 import (e4m3_decode, dequantise, attention_fp8_reference, fp8_output_bound, fp8_score_error_bound,
                   fp8_float32_bound, summation_gamma)
+from .mxfp4 import e2m1_decode, e8m0_decode, mx_decode, attention_mxfp4_reference, mxfp4_bounds
 from . import roofline
 
 __all__ = [
@@ -56,4 +60,5 @@ __all__ = [
     "relative_error_curve", "attention_partial", "merge_partials", "roofline",
     "e4m3_decode", "dequantise", "attention_fp8_reference", "fp8_output_bound", "fp8_score_error_bound",
     "fp8_float32_bound", "summation_gamma",
+    "e2m1_decode", "e8m0_decode", "mx_decode", "attention_mxfp4_reference", "mxfp4_bounds",
 ]

@@ -105,10 +105,9 @@ def attention_fp8_reference(q8, k8, v8, q_descale, k_descale, v_descale, scale, 
                              scale, causal)
 
 
-def fp8_output_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
-    """Per-element bound [B,H,Sq,d] on |O_kernel - O_exact| from rounding the
-    unnormalised probabilities to e4m3 (see the module text)."""
-    q, k, v = dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale)
+def output_bound_of(q, k, v, scale, causal=False):
+    """fp8_output_bound on dequantised float arrays q, k, v (any operand
+    format whose P is rounded to e4m3 before P V)."""
     p = attention_probs(q, k, scale, causal)                 # exact softmax weights
     av = np.abs(_f64(v))
     rel = np.einsum("bhij,bhjc->bhic", p, av)                # sum_j p_j |v_j|
@@ -120,11 +119,16 @@ def fp8_output_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=
     return 2.0 ** -4 * rel + 2.0 ** -10 * absum / lmax
 
 
-def fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal=False):
-    """Per-row bound [B,H,Sq] on the float32 accumulation error of the row's
-    scores (and so of its LSE): gamma_d * scale * max over visible keys of
-    sum_c |q_c k_c| on the dequantised inputs (see the module text)."""
-    q, k = np.abs(dequantise(q8, q_descale)), np.abs(dequantise(k8, k_descale))
+def fp8_output_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
+    """Per-element bound [B,H,Sq,d] on |O_kernel - O_exact| from rounding the
+    unnormalised probabilities to e4m3 (see the module text)."""
+    return output_bound_of(dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale),
+                           scale, causal)
+
+
+def score_error_bound_of(q, k, scale, causal=False):
+    """fp8_score_error_bound on dequantised float arrays q, k."""
+    q, k = np.abs(_f64(q)), np.abs(_f64(k))
     d = q.shape[-1]
     u = 2.0 ** -24
     gamma = d * u / (1.0 - d * u)
@@ -133,6 +137,13 @@ def fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal=False):
         Sq, Sk = ab.shape[-2:]
         ab = np.where(np.tril(np.ones((Sq, Sk), dtype=bool)), ab, 0.0)
     return gamma * scale * ab.max(axis=-1)
+
+
+def fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal=False):
+    """Per-row bound [B,H,Sq] on the float32 accumulation error of the row's
+    scores (and so of its LSE): gamma_d * scale * max over visible keys of
+    sum_c |q_c k_c| on the dequantised inputs (see the module text)."""
+    return score_error_bound_of(dequantise(q8, q_descale), dequantise(k8, k_descale), scale, causal)
 
 
 U32 = 2.0 ** -24
@@ -148,17 +159,22 @@ def summation_gamma(n, lam=10.0):
     return np.minimum(worst, prob)
 
 
-def fp8_float32_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
-    """Per-element bound [B,H,Sq,d] on what float32 arithmetic adds to the
-    kernel's O error beside the rounding of P (see the module text)."""
-    q, k, v = dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale)
+def float32_bound_of(q, k, v, scale, causal=False):
+    """fp8_float32_bound on dequantised float arrays q, k, v."""
     p = attention_probs(q, k, scale, causal)
     rel = np.einsum("bhij,bhjc->bhic", p, np.abs(_f64(v)))        # sum_j p_j |v_j|
     Sq, Sk = p.shape[-2], p.shape[-1]
     vis = np.tril(np.ones((Sq, Sk), dtype=bool)) if causal else np.ones((Sq, Sk), dtype=bool)
     s_abs = np.abs(scale * np.einsum("bhic,bhjc->bhij", _f64(q), _f64(k)))
     smax = np.where(vis, s_abs, 0.0).max(axis=-1)
-    eps = fp8_score_error_bound(q8, k8, q_descale, k_descale, scale, causal) + 8.0 * U32 * smax
+    eps = score_error_bound_of(q, k, scale, causal) + 8.0 * U32 * smax
     n = vis.sum(axis=-1).astype(np.float64)                          # [Sq]
     factor = np.expm1(2.0 * eps) + 2.0 * summation_gamma(n) + 16.0 * U32
     return factor[..., None] * rel
+
+
+def fp8_float32_bound(q8, k8, v8, q_descale, k_descale, v_descale, scale, causal=False):
+    """Per-element bound [B,H,Sq,d] on what float32 arithmetic adds to the
+    kernel's O error beside the rounding of P (see the module text)."""
+    return float32_bound_of(dequantise(q8, q_descale), dequantise(k8, k_descale), dequantise(v8, v_descale),
+                            scale, causal)

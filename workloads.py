@@ -110,3 +110,32 @@ def quantise_e4m3_per_head(x, amax=224.0):
     descale = torch.where(m > 0, m / amax, torch.ones_like(m))
     codes = (x.float() / descale[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, descale
+
+
+_E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantise_mxfp4(x, block=32):
+    """MXFP4 codes of a float tensor [..., d] (d a multiple of 2 * block/2):
+    per block of `block` consecutive elements of a row, the shared exponent
+    X = floor(log2(max |x|)) - 2 (the OCP microscaling rule for E2M1, whose
+    largest exponent is 2), stored as the E8M0 byte X + 127; each element
+    x / 2^X goes to the nearest E2M1 value (ties to the even code), saturating
+    at +-6.  Returns (packed uint8 [..., d/2], element 2j in the low nibble of
+    byte j; scales uint8 [..., d/block])."""
+    xf = x.float()
+    shp = xf.shape
+    blocks = xf.reshape(shp[:-1] + (shp[-1] // block, block))
+    amax = blocks.abs().amax(dim=-1, keepdim=True)
+    X = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0))
+    X = X.clamp(-127, 127)
+    y = (blocks / torch.exp2(X)).reshape(shp)
+    mags = torch.tensor(_E2M1_MAGS, dtype=torch.float32)
+    dist = (y.abs().clamp(max=6.0)[..., None] - mags).abs()
+    # nearest magnitude; on a tie the even code (mantissa bit 0) wins
+    dist = dist + 1e-6 * (torch.arange(8) & 1).float()
+    idx = dist.argmin(dim=-1)
+    codes = (idx | torch.where(y < 0, 8, 0)).to(torch.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).to(torch.uint8).contiguous()
+    scales = (X.squeeze(-1) + 127).to(torch.uint8).contiguous()
+    return packed, scales
