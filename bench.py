@@ -37,6 +37,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA, twice the bf16 rate
+PEAK_FP4_TFLOPS = 10066.3     # MI355X dense fp4 MFMA, four times the bf16 rate
+# the MXFP4 forward: half its counted FLOPs (S = Q K^T) at the fp4 rate, half
+# (P V) at the fp8 rate -> the time-weighted peak of the mix
+PEAK_MXFP4_MIX_TFLOPS = 1.0 / (0.5 / PEAK_FP4_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -62,6 +66,8 @@ def parse():
                         "(a known byte count that scales the HBM counters)")
     p.add_argument("--fp8", action="store_true",
                    help="with --reps and --fwd-only: run the e4m3 forward on the quantised workload")
+    p.add_argument("--mxfp4", action="store_true",
+                   help="with --reps and --fwd-only: run the MXFP4 forward (MXFP4 Q, K; e4m3 V)")
     return p.parse_args()
 
 
@@ -208,6 +214,17 @@ def main():
 
             def fwd():
                 fa.fa_fwd_fp8(q8, k8, v8, o, lse, qs, ks, vs, causal=w.causal, scale=w.scale, tau=args.tau)
+        elif args.mxfp4:
+            if do_bwd:
+                sys.exit("--mxfp4 profiles the forward only: add --fwd-only")
+            from workloads import quantise_e4m3, quantise_mxfp4
+            q4, q4s = (t.to(dev) for t in quantise_mxfp4(q.cpu()))
+            k4, k4s = (t.to(dev) for t in quantise_mxfp4(k.cpu()))
+            v8, vs = quantise_e4m3(v.cpu())
+            v8 = v8.to(dev)
+
+            def fwd():
+                fa.fa_fwd_mxfp4(q4, q4s, k4, k4s, v8, o, lse, vs, causal=w.causal, scale=w.scale, tau=args.tau)
         if args.copy_mib:
             src = torch.ones(args.copy_mib * 2**20 // 4, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
@@ -221,6 +238,7 @@ def main():
                 bwd()
         torch.cuda.synchronize()
         print(f"ran {args.reps} steps of {w.name}" + (" (e4m3 forward)" if args.fp8 else "") +
+              (" (MXFP4 forward)" if args.mxfp4 else "") +
               (f" after {args.reps} copies of {args.copy_mib} MiB" if args.copy_mib else ""), flush=True)
         return
 
@@ -322,7 +340,52 @@ def main():
                     extra[f"{ww.name}-fp8-tau0"] = {
                         "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3", "tau": 0.0,
                         "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
-                del q8, k8, v8
+                # MXFP4 Q and K (E8M0 scales per 32 dims), e4m3 V: S on the
+                # scaled fp4 products, P V in e4m3
+                from workloads import quantise_mxfp4
+                q4, q4s = (t.to(dev) for t in quantise_mxfp4(qq.cpu()))
+                k4, k4s = (t.to(dev) for t in quantise_mxfp4(kk.cpu()))
+                ms = time_calls(lambda: fa.fa_fwd_mxfp4(q4, q4s, k4, k4s, v8, oo, ll, vs, causal=ww.causal,
+                                                        scale=ww.scale, tau=args.tau),
+                                max(10, args.steps), 3, args.warm_seconds / 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}-mxfp4"] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "mxfp4 q,k / e4m3 v,p",
+                    "pct_peak_mix": round(100 * tf / PEAK_MXFP4_MIX_TFLOPS, 2),
+                    "peak_tflops": round(PEAK_MXFP4_MIX_TFLOPS, 1),
+                    "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
+                del q8, k8, v8, q4, q4s, k4, k4s
+            if wid == 3:
+                # the graded forward's own roofline: algorithmic 4 d FLOPs per
+                # counted (query, key) pair over its event-timed launch
+                ms3 = extra[ww.name]["ms"]
+                work3 = ww.flops("fwd")
+                ach = work3 / (ms3 * 1e-3) / 1e12
+                extra[f"{ww.name}-roofline"] = {
+                    "bound": "mfma", "kernel": "fwd_kernel", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": read_traffic("fwd_kernel", ww.name), "work_per_launch": work3,
+                    "avg_launch_ms": ms3}
+            if wid in (3, 4):
+                # the conditional rescale observed: wavefront-level corrections
+                # after each wavefront's first tile (instrumented forward), at
+                # tau = 8 and at tau = 0 (every rise of a wavefront's max)
+                ev = torch.zeros((ww.B, ww.H), dtype=torch.int32, device=dev)
+                counts = {}
+                for tau_c in (8.0, 0.0):
+                    ev.zero_()
+                    fa.fa_fwd_rescale_count(qq, kk, vv, oo, ll, ev, causal=ww.causal, scale=ww.scale, tau=tau_c)
+                    torch.cuda.synchronize()
+                    counts[f"tau{tau_c:g}"] = int(ev.sum().item())
+                # (wavefront, tile) steps after the first: each 32-row wavefront
+                # visits ceil(visible keys / 128) tiles of 128 keys
+                import math as _m
+                steps = 0
+                for w0 in range(0, ww.Sq, 32):
+                    last = min(ww.Sk, w0 + 32) if ww.causal else ww.Sk
+                    steps += _m.ceil(last / 128) - 1
+                counts["wave_tile_steps_after_first"] = steps * ww.B * ww.H
+                extra[f"{ww.name}-rescale_events"] = counts
             if wid == 4:
                 # ablation of the conditional rescale: tau = 0 corrects the
                 # output on every increase of a row max (the eager online softmax)
@@ -363,6 +426,16 @@ def main():
             "merge_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": merge_bytes}}
         del qq, kk, vv, op, lp, om, lm
+
+    if do_bwd and not args.no_extra:
+        # the deterministic flag selects the same kernels (every output element
+        # is written once by one workgroup in a fixed order): both timed
+        det_ab = {}
+        for det in (0, 1):
+            det_ab[f"deterministic{det}_bwd_ms"] = round(time_calls(
+                lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
+                                  deterministic=bool(det)), max(10, args.steps), 3, args.warm_seconds / 3), 5)
+        extra["bwd_deterministic_ab"] = det_ab
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
     "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
-    "backward", "fa_bwd_noalloc", "LIB_PATH",
+    "backward", "fa_bwd_noalloc", "fa_fwd_mxfp4", "forward_mxfp4", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -50,6 +50,8 @@ def lib():
     L.fa_fwd_rescale_count.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
     L.fa_fwd_fp8.restype = i
+    L.fa_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, f, f, vp]
+    L.fa_fwd_mxfp4.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
     L.fa_fwd_partial.restype = i
     L.fa_merge.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
@@ -180,6 +182,47 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, 
                           _stream(q8))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
+
+
+def _check_u8(name, t, shape):
+    import torch
+    if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous uint8 CUDA tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def fa_fwd_mxfp4(q4, q_scales, k4, k_scales, v8, o, lse, v_descale=1.0, causal=False, scale=None, tau=8.0):
+    """Enqueue the MXFP4-Q/K, e4m3-V forward: q4 [B,H,Sq,d/2] and k4
+    [B,H,Sk,d/2] packed E2M1 bytes, q_scales [B,H,Sq,d/32] and k_scales
+    [B,H,Sk,d/32] E8M0 bytes, v8 e4m3 [B,H,Sk,d]; fills the bf16 o and
+    float32 lse in place."""
+    B, H, Sq, d2 = q4.shape
+    d = 2 * d2
+    Sk = k4.shape[2]
+    _check_u8("q4", q4, (B, H, Sq, d2))
+    _check_u8("k4", k4, (B, H, Sk, d2))
+    _check_u8("q_scales", q_scales, (B, H, Sq, d // 32))
+    _check_u8("k_scales", k_scales, (B, H, Sk, d // 32))
+    _check_e4m3("v8", v8, (B, H, Sk, d))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_mxfp4(_ptr(q4), _ptr(q_scales), _ptr(k4), _ptr(k_scales), _ptr(v8), float(v_descale),
+                            _ptr(o), _ptr(lse), B, H, Sq, Sk, d, int(bool(causal)), float(scale), float(tau),
+                            _stream(q4))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_mxfp4")
+
+
+def forward_mxfp4(q4, q_scales, k4, k_scales, v8, v_descale=1.0, causal=False, scale=None, tau=8.0):
+    """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq]) of the MXFP4 forward."""
+    import torch
+    B, H, Sq, d2 = q4.shape
+    o = torch.empty((B, H, Sq, 2 * d2), dtype=torch.bfloat16, device=q4.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q4.device)
+    fa_fwd_mxfp4(q4, q_scales, k4, k_scales, v8, o, lse, v_descale, causal=causal, scale=scale, tau=tau)
+    return o, lse
 
 
 def fa_fwd_partial(q, k, v, o_part, lse_part, q_offset, k_begin, k_end, causal=False, scale=None, tau=8.0,

@@ -133,6 +133,36 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_mxfp4(const void* Q4, const void* Q_scales, const void* K4, const void* K_scales, const void* V8,
+                        float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal,
+                        float scale, float tau, void* stream) {
+  if (!Q4 || !Q_scales || !K4 || !K_scales || !V8 || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(Q4) || !aligned16(K4) || !aligned16(V8) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(Q_scales) & 3u) != 0 || (reinterpret_cast<uintptr_t>(K_scales) & 3u) != 0)
+    return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(v_descale) && v_descale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(scale * 1.4426950408889634f) && scale * 1.4426950408889634f >= FLT_MIN)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdFp8Args a;
+  a.q = Q4; a.k = K4; a.v = V8; a.o = O; a.lse = LSE;
+  a.q_scales = Q_scales; a.k_scales = K_scales;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.q_descale = 1.0f; a.k_descale = 1.0f; a.v_descale = v_descale;
+  a.head_descales = nullptr;
+  a.tau = tau;
+  const hipError_t e = fa::launch_fwd_mxfp4(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_partial(const void* Q, const void* K, const void* V, float* O_part, float* LSE_part, int B, int H,
                          int Sq, int Sk, int d, int q_offset, int k_begin, int k_end, int causal, float scale,
                          float tau, float emu_frac, void* stream) {

@@ -53,16 +53,19 @@ constexpr int kD8 = 128;                 // head dimension = bytes per row
 constexpr int kTile8 = kBN8 * kD8;       // 16 KiB
 constexpr int kRing8 = 4 * kTile8;       // K stages 0, 1 then V stages 0, 1
 constexpr int kLds8 = kRing8 > kWaves8 * RowStore<kD8>::kBytes ? kRing8 : kWaves8 * RowStore<kD8>::kBytes;
+static_assert(2 * (kTile8 / 2 + kBN8 * 4) + 2 * kTile8 <= kLds8, "MXFP4 ring exceeds the LDS allocation");
 constexpr int kAhead8 = 2;               // operands in flight per wave (64-cycle products)
 
 struct Fwd8Params {
-  const uint8_t* q;
-  const uint8_t* k;
+  const uint8_t* q;      // e4m3 [BH, Sq, 128], or MXFP4 elements [BH, Sq, 64]
+  const uint8_t* k;      // e4m3 [BH, Sk, 128], or MXFP4 elements [BH, Sk, 64]
   const uint8_t* v;
+  const uint8_t* qsc;    // MXFP4 only: E8M0 scales [BH, Sq, 4] and [BH, Sk, 4]
+  const uint8_t* ksc;
   bf16* o;
   float* lse;
   int BH, Sq, Sk, n_qblocks;
-  float s_log2;      // scale * q_descale * k_descale * log2(e)
+  float s_log2;      // scale * q_descale * k_descale * log2(e) (MXFP4: scale * log2(e))
   float v_descale;
   const float* hd;   // null, or per-slice factors [3][BH] (q, k, v)
   float tau;
@@ -88,6 +91,40 @@ __device__ __forceinline__ void drain8(f32x16& a, f32x16& b, f32x16& c, f32x16& 
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// MXFP4 x MXFP4 products (E2M1 elements, 4 VGPRs per operand) with E8M0
+// block scales: v_mfma_scale_f32_32x32x64_f8f6f4 with cbsz = blgp = 4 (both
+// operands E2M1).  Lane l's 32 elements (k = 32 (l / 32) .. +31 of the 64)
+// are one microscaling block; each scale operand holds the lanes' scale bytes
+// of k-step kc in byte kc, selected by op_sel (low bit of the byte index) and
+// op_sel_hi (high bit).  Checked on MI355X against a float64 product of
+// random E2M1 codes with random per-lane scales.  The same hazards as
+// mfma8_acc; drain8() covers these products too.
+// k-step 1 (byte 1 of each scale operand), accumulating
+__device__ __forceinline__ void mfma4_acc1(f32x16& d, const i32x4& a, const i32x4& b, uint32_t sa, uint32_t sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[1,1,0] op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+               : "+v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// k-step 0 (byte 0), from zero
+__device__ __forceinline__ void mfma4_init(f32x16& d, const i32x4& a, const i32x4& b, uint32_t sa, uint32_t sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+               : "=&v"(d) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// MXFP4 K tiles: 128 rows of 64 bytes (128 E2M1 elements), the 16-byte chunk
+// c of row r at byte r * 64 + 16 * (c ^ swz4(r)), so 16 consecutive rows read
+// at one chunk meet 16 distinct 16-byte bank slots; then the rows' E8M0
+// scale dwords (4 blocks of 32 dims each), 128 x 4 bytes.
+constexpr int kRow4 = kD8 / 2;                 // bytes per MXFP4 row
+constexpr int kTileK4 = kBN8 * kRow4;          // 8 KiB
+constexpr int kStageK4 = kTileK4 + kBN8 * 4;   // + scale dwords
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
+
+// The lane's scale bytes for the two 64-dim k-steps (byte kc = block 2 kc + g,
+// g = lane / 32) out of a row's 4 scale bytes.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t row_scales, int g) {
+  return __builtin_amdgcn_perm(0u, row_scales, g ? 0x0c0c0301u : 0x0c0c0200u);
+}
+
 // k-slot j of lane group g (0, 1) -> key of the 64-key step
 __device__ __forceinline__ int slot_key(int g, int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * g + (j % 4); }
 
@@ -103,7 +140,20 @@ __device__ __forceinline__ void dma_tile8(__amdgpu_buffer_rsrc_t src, int row0, 
   }
 }
 
-template <bool CAUSAL>
+// an MXFP4 K tile memory-to-LDS: one 16-byte load per lane covers 16 rows
+// (each wave one of the 8), then the scale dwords of its 128 rows (waves 0
+// and 1, 64 rows each)
+__device__ __forceinline__ void dma_tile4(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t ssrc, int row0, char* tile,
+                                          int wave, int lane) {
+  const int blk = wave;   // wave-uniform
+  const int row = blk * 16 + lane / 4;
+  const unsigned off = (unsigned)(row0 + row) * kRow4 + 16 * ((lane % 4) ^ swz4(row));
+  lds_dma16(src, off, tile + blk * 16 * kRow4);
+  if (wave < 2) lds_dma4(ssrc, (unsigned)(row0 + 64 * wave + lane) * 4, tile + kTileK4 + 64 * wave * 4);
+}
+
+// FP4QK: Q and K in MXFP4 (S^T on the scaled fp4 products), V and P in e4m3.
+template <bool CAUSAL, bool FP4QK = false>
 __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   constexpr int kKB = kBN8 / 32;   // 32-key blocks of S^T per tile
   constexpr int kKC = kD8 / 64;    // 64-dim steps of S^T
@@ -128,8 +178,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     v_descale *= p.hd[2 * p.BH + bh];
   }
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * kD8, (unsigned)p.Sq * kD8);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
+  constexpr int kRowQK = FP4QK ? kRow4 : kD8;   // bytes per Q / K row
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * kRowQK, (unsigned)p.Sq * kRowQK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * kRowQK, (unsigned)p.Sk * kRowQK);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
 
   const int q_wave_lo = qb * kBM8 + wave * kQW8;
@@ -137,10 +188,25 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 
   // Q^T operand, k-step kc: lane holds Q[q_lane][64 kc + 32 g .. +31]
   i32x8 qf[kKC];
+  // MXFP4: lane holds the 32 elements Q[q_lane][64 kc + 32 g .. +31] (16
+  // bytes) per k-step, and the scale bytes of those blocks (byte kc)
+  i32x4 qf4[kKC];
+  uint32_t q_sc = 0;
+  __amdgpu_buffer_rsrc_t rks = rk;
+  if constexpr (FP4QK) {
 #pragma unroll
-  for (int kc = 0; kc < kKC; ++kc) {
-    qf[kc].lo = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g));
-    qf[kc].hi = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g + 16));
+    for (int kc = 0; kc < kKC; ++kc)
+      qf4[kc] = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kRow4 + 32 * kc + 16 * g));
+    const __amdgpu_buffer_rsrc_t rqs = make_rsrc(p.qsc + (size_t)bh * p.Sq * 4, (unsigned)p.Sq * 4);
+    const uint32_t qrow = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, (int)((unsigned)q_lane * 4), 0, 0);
+    q_sc = scale_pair(qrow, g);
+    rks = make_rsrc(p.ksc + (size_t)bh * p.Sk * 4, (unsigned)p.Sk * 4);
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < kKC; ++kc) {
+      qf[kc].lo = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g));
+      qf[kc].hi = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g + 16));
+    }
   }
 
   // K operand addresses: row 32 kb + r32 has the chunk permutation of r32
@@ -189,8 +255,17 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   float m_ref = kNegInf;
   float l_part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto k_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (u & 1) * kTile8; };
-  auto v_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (2 + (u & 1)) * kTile8; };
+  // LDS ring: K stages 0, 1 then V stages 0, 1 (MXFP4 K stages are half a
+  // tile plus the scale dwords)
+  constexpr int kStageK = FP4QK ? kStageK4 : kTile8;
+  auto k_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (u & 1) * kStageK; };
+  auto v_stage = [&](int u) __attribute__((always_inline)) -> char* {
+    return smem + 2 * kStageK + (u & 1) * kTile8;
+  };
+  // MXFP4 K operand: row 32 kb + r32, bytes 32 kc + 16 g .. +15 (chunk 2 kc + g)
+  int k4_off[2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) k4_off[kc] = r32 * kRow4 + 16 * ((2 * kc + g) ^ swz4(r32));
 
   // ---- matrix phase: O^T += V^T P^T of tile uv, then S^T = K Q^T of tile uk
   auto matrix_stream_body = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
@@ -217,12 +292,25 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
       }
       const int i = j - kNV;
       const int kb = i % kKB, kc = i / kKB;
-      const char* row = kst + kb * 32 * kD8;
       i32x8 r;
-      r.lo = *reinterpret_cast<const i32x4*>(row + k_off[kc][0]);
-      r.hi = *reinterpret_cast<const i32x4*>(row + k_off[kc][1]);
+      if constexpr (FP4QK) {
+        // 16 bytes (32 elements) per lane; the upper half of the ring entry is unused
+        r.lo = *reinterpret_cast<const i32x4*>(kst + kb * 32 * kRow4 + k4_off[kc]);
+      } else {
+        const char* row = kst + kb * 32 * kD8;
+        r.lo = *reinterpret_cast<const i32x4*>(row + k_off[kc][0]);
+        r.hi = *reinterpret_cast<const i32x4*>(row + k_off[kc][1]);
+      }
       return r;
     };
+    // MXFP4: the scale bytes of the K rows of each 32-key block (byte kc = the
+    // lane's block of k-step kc)
+    uint32_t k_sc[kKB];
+    if constexpr (FP4QK && SK) {
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+        k_sc[kb] = scale_pair(*reinterpret_cast<const uint32_t*>(kst + kTileK4 + (32 * kb + r32) * 4), g);
+    }
     i32x8 ring[kAhead8];
 #pragma unroll
     for (int j = j0; j < j0 + kAhead8 && j < j1; ++j) ring[(j - j0) % kAhead8] = operand(j);
@@ -234,10 +322,17 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
         mfma8_acc(o[j % kDB], a, pk[j / kDB]);
       } else {
         const int i = j - kNV;   // the first k-step starts each accumulator
-        if (i < kKB)
-          mfma8_init(s[i % kKB], a, qf[i / kKB]);
-        else
-          mfma8_acc(s[i % kKB], a, qf[i / kKB]);
+        if constexpr (FP4QK) {
+          if (i < kKB)
+            mfma4_init(s[i % kKB], a.lo, qf4[0], k_sc[i % kKB], q_sc);
+          else
+            mfma4_acc1(s[i % kKB], a.lo, qf4[1], k_sc[i % kKB], q_sc);
+        } else {
+          if (i < kKB)
+            mfma8_init(s[i % kKB], a, qf[i / kKB]);
+          else
+            mfma8_acc(s[i % kKB], a, qf[i / kKB]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -295,7 +390,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   // ---- tile IO: interval 2u-1 issues K_u and V_{u-1}; the end of every even
   // interval waits for them (the schedule of the bf16 256-row form)
   auto fetch = [&](int u) __attribute__((always_inline)) {
-    if (u < n) dma_tile8(rk, u * kBN8, k_stage(u), wave, lane);
+    if (u < n) {
+      if constexpr (FP4QK) dma_tile4(rk, rks, u * kBN8, k_stage(u), wave, lane);
+      else dma_tile8(rk, u * kBN8, k_stage(u), wave, lane);
+    }
     if (u >= 1 && u <= n) dma_tile8(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
   };
   auto commit = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -409,6 +507,34 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
     return hipGetLastError();
   };
   return a.causal ? run(fwd8_kernel<true>) : run(fwd8_kernel<false>);
+}
+
+hipError_t launch_fwd_mxfp4(const FwdFp8Args& a, hipStream_t stream) {
+  Fwd8Params prm;
+  prm.q = static_cast<const uint8_t*>(a.q);
+  prm.k = static_cast<const uint8_t*>(a.k);
+  prm.v = static_cast<const uint8_t*>(a.v);
+  prm.qsc = static_cast<const uint8_t*>(a.q_scales);
+  prm.ksc = static_cast<const uint8_t*>(a.k_scales);
+  prm.o = static_cast<bf16*>(a.o);
+  prm.lse = a.lse;
+  prm.BH = a.B * a.H;
+  prm.Sq = a.Sq;
+  prm.Sk = a.Sk;
+  prm.n_qblocks = (a.Sq + kBM8 - 1) / kBM8;
+  prm.s_log2 = a.scale * kLog2e;
+  prm.v_descale = a.v_descale;
+  prm.hd = nullptr;
+  prm.tau = a.tau;
+  const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
+  auto run = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds8);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads8), kLds8, stream, prm);
+    return hipGetLastError();
+  };
+  return a.causal ? run(fwd8_kernel<true, true>) : run(fwd8_kernel<false, true>);
 }
 
 }  // namespace fa

@@ -45,8 +45,13 @@ struct FwdFp8Args {
   bool causal;
   float scale, q_descale, k_descale, v_descale, tau;
   const float* head_descales;   // null or [3][B*H] on the device
+  const void* q_scales = nullptr;   // MXFP4: E8M0 scales [B*H][Sq][4], [B*H][Sk][4]
+  const void* k_scales = nullptr;
 };
 hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
+// MXFP4 Q, K (E2M1 elements, d/2 bytes per row; E8M0 scales per 32 dims),
+// e4m3 V: q_descale and k_descale unused, head_descales null
+hipError_t launch_fwd_mxfp4(const FwdFp8Args& a, hipStream_t stream);
 
 // rows = B * H * Sq; parts are n_parts consecutive [rows, d] / [rows] arrays
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int rows, int d, void* o,

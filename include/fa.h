@@ -116,6 +116,28 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
                      float v_descale, const float* head_descales, void* O, float* LSE, int B, int H, int Sq,
                      int Sk, int d, int causal, float scale, float tau, void* stream);
 
+/* Forward with MXFP4 queries and keys and e4m3 values: the FP4 operand
+ * experiment of the lecture notes "How FlashAttention 4 Works" (FP4 among
+ * Blackwell's new formats, experimental in their map of which attention
+ * operands tolerate which precision, FP4 channels among the open questions).
+ * Q4 and K4 hold MXFP4 rows: d/2 bytes per row, two E2M1 elements per byte
+ * (the even-indexed element in the low nibble; E2M1 = sign, 2-bit exponent
+ * with bias 1, 1-bit mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), layout
+ * [B,H,Sq,d/2] and [B,H,Sk,d/2]; Q_scales and K_scales hold one E8M0 byte
+ * (2^(s - 127)) per 32 consecutive elements of a row, [B,H,Sq,d/32] and
+ * [B,H,Sk,d/32] (4-byte aligned); V8 is e4m3 [B,H,Sk,d] with one descale.
+ * The attention is computed on the decoded tensors: S = scale * Q K^T from
+ * scaled fp4 x fp4 products with float32 accumulation, P = 2^(s - m_ref)
+ * rounded to e4m3 before P V (as in fa_fwd_fp8), row sum and LSE from the
+ * float32 P.  O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq].
+ *   d = 128 only (else FA_ERR_UNSUPPORTED); 0 <= tau <= 8; v_descale finite
+ *   and > 0; causal requires Sq = Sk; other arguments and errors as for
+ *   fa_fwd.  Scale bytes of 255 (NaN) give non-finite outputs.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+fa_status fa_fwd_mxfp4(const void* Q4, const void* Q_scales, const void* K4, const void* K_scales, const void* V8,
+                       float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal,
+                       float scale, float tau, void* stream);
+
 /* Forward over a range of keys, for split-KV and ring (context-parallel)
  * attention: queries i = 0 .. Sq-1 of Q (global index q_offset + i) attend to
  * the keys j = k_begin .. k_end-1 of K, V only (causal: key j is visible iff

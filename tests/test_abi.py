@@ -186,3 +186,24 @@ def test_bwd_noalloc_validation(L):
     assert call(B=2, H=16, Sq=limit // 32 + 1, Sk=limit // 32 + 1) == fa.FA_ERR_SCRATCH
     assert call(B=1, H=1, Sq=limit + 1, Sk=limit + 1, causal=0) == fa.FA_ERR_SCRATCH
     assert "scratch" in fa.fa_status_str(fa.FA_ERR_SCRATCH)
+
+
+def test_fwd_mxfp4_rejects_before_any_launch(L):
+    vp = ctypes.c_void_p
+
+    def call(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, vd=1.0, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=16, d=128,
+             causal=0, scale=0.125, tau=8.0):
+        return L.fa_fwd_mxfp4(vp(q), vp(qs), vp(k), vp(ks), vp(v), vd, vp(o), vp(lse), B, H, Sq, Sk, d, causal,
+                              scale, tau, vp(0))
+    assert call(qs=0) == fa.FA_ERR_INVALID
+    assert call(k=0) == fa.FA_ERR_INVALID
+    assert call(ks=FAKE + 2) == fa.FA_ERR_INVALID          # scales must be 4-byte aligned
+    assert call(q=FAKE + 8) == fa.FA_ERR_INVALID
+    assert call(vd=0.0) == fa.FA_ERR_INVALID
+    assert call(vd=float("inf")) == fa.FA_ERR_INVALID
+    assert call(tau=9.0) == fa.FA_ERR_INVALID
+    assert call(scale=-1.0) == fa.FA_ERR_INVALID
+    assert call(scale=1e-40) == fa.FA_ERR_INVALID           # scale * log2(e) below the normal range
+    assert call(causal=2) == fa.FA_ERR_INVALID
+    assert call(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=1, Sk=32) == fa.FA_ERR_UNSUPPORTED

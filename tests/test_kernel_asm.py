@@ -201,6 +201,16 @@ def test_fp8_products_drained_before_any_other_use(src, kernel_assembly):
     assert not bad, "accumulator used before the drain:\n" + "\n".join(bad[:20])
 
 
+@pytest.mark.parametrize("src", [s for s in KERNEL_SOURCES if os.path.basename(s) == "fa_fwd8.hip"],
+                         ids=os.path.basename)
+def test_mxfp4_products_drained_before_any_other_use(src, kernel_assembly):
+    """The scaled fp4 products of the MXFP4 forward are inline asm too."""
+    asm = kernel_assembly[src]
+    assert asm.count("v_mfma_scale_f32_32x32x64_f8f6f4") >= 8
+    bad = early_accumulator_reads(asm, mnemonic="v_mfma_scale_f32_32x32x64_f8f6f4")
+    assert not bad, "accumulator used before the drain:\n" + "\n".join(bad[:20])
+
+
 def test_drain_scanner_finds_a_planted_copy():
     planted = "\n".join([
         "\tv_mfma_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], v[0:15]",
