@@ -20,9 +20,10 @@
 //   * products v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3, scales 1): A and
 //     B lanes hold 32 consecutive k (lane l: row l % 32, k 32 (l / 32) .. +31);
 //     the C layout is the bf16 32x32 one, so the softmax code is unchanged;
-//   * e4m3 tiles of 128 keys x 128 bytes; the 16-byte chunk c of row r sits at
-//     chunk position c ^ ((r >> 1) & 7), so 16 consecutive rows read at one
-//     chunk meet 16 distinct 16-byte bank slots;
+//   * e4m3 tiles of 128 keys x 128 bytes; the 16-byte chunk c of K row r sits
+//     at chunk position c ^ ((r >> 1) & 7), so 16 consecutive rows read at one
+//     chunk meet 16 distinct 16-byte bank slots; V rows have a permutation of
+//     their own that suits the rows a transposed read touches (swzv);
 //   * S^T = K Q^T: K is the A operand (two 16-byte reads of one row), Q^T the
 //     B operand in registers;
 //   * O^T += V^T P^T per 64 keys: P^T (B operand) is two S^T accumulators
@@ -71,8 +72,17 @@ struct Fwd8Params {
   float tau;
 };
 
-// the 16-byte chunk c of tile row r sits at byte r * kD8 + 16 * (c ^ swz8(r))
+// the 16-byte chunk c of K tile row r sits at byte r * kD8 + 16 * (c ^ swz8(r)):
+// the 16 consecutive rows one 16-byte read instruction meets at chunk c land
+// on 16 distinct 16-byte bank slots (even and odd rows fall in opposite
+// halves of the 64 banks, and (r >> 1) & 7 spreads each half's 8 rows)
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// V tiles: chunk c of row r at c ^ swzv(r).  A V^T read's 32 lanes of one
+// pass address rows r0, r0 + 2, r0 + 8, r0 + 10 of each parity (r0 in
+// {0, 1, 4, 5} + 16 k), two 16-byte chunks 2 db, 2 db + 1 each; row bits 1
+// and 3 select the chunk pair, so the four rows of a parity cover the 8 bank
+// slots of their half once (swz8 maps them to two pairs: a 2-way conflict)
+__device__ __forceinline__ int swzv(int r) { return (r & 2) | ((r >> 1) & 4); }
 
 // e4m3 x e4m3 products written out as single instructions (the compiler
 // moves its own form of this product past barriers to the first use of the
@@ -128,14 +138,17 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t row_scales, int g) {
 // k-slot j of lane group g (0, 1) -> key of the 64-key step
 __device__ __forceinline__ int slot_key(int g, int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * g + (j % 4); }
 
-// a tile of 128 rows, memory-to-LDS with the chunk permutation: one 16-byte
-// load per lane covers 8 whole rows; a wave issues 2 of the 16
+// a tile of 128 rows, memory-to-LDS with the chunk permutation (swz8 for K,
+// swzv for V): one 16-byte load per lane covers 8 whole rows; a wave issues
+// 2 of the 16
+template <bool V_TILE>
 __device__ __forceinline__ void dma_tile8(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < kBN8 / 8 / kWaves8; ++i) {
     const int blk = i * kWaves8 + wave;   // wave-uniform
     const int row = blk * 8 + lane / 8;
-    const unsigned off = (unsigned)(row0 + row) * kD8 + 16 * ((lane % 8) ^ swz8(row));
+    const int sw = V_TILE ? swzv(row) : swz8(row);
+    const unsigned off = (unsigned)(row0 + row) * kD8 + 16 * ((lane % 8) ^ sw);
     lds_dma16(src, off, tile + blk * 8 * kD8);
   }
 }
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = slot_key(g, 8 * q + m8);
-    const int sw = swz8(row);
+    const int sw = swzv(row);
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
       v_off[q][db] = row * kD8 + 8 * par + 16 * (half ^ (sw & 1)) + ((32 * db) ^ (32 * (sw >> 1)));
@@ -392,9 +405,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   auto fetch = [&](int u) __attribute__((always_inline)) {
     if (u < n) {
       if constexpr (FP4QK) dma_tile4(rk, rks, u * kBN8, k_stage(u), wave, lane);
-      else dma_tile8(rk, u * kBN8, k_stage(u), wave, lane);
+      else dma_tile8<false>(rk, u * kBN8, k_stage(u), wave, lane);
     }
-    if (u >= 1 && u <= n) dma_tile8(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
+    if (u >= 1 && u <= n) dma_tile8<true>(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
   };
   auto commit = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto barrier = [&]() __attribute__((always_inline)) {
