@@ -51,6 +51,7 @@ from .partial import attention_partial, merge_partials
 from .fp8 import (e4m3_decode, dequantise, attention_fp8_reference, fp8_output_bound, fp8_score_error_bound,
                   fp8_float32_bound, summation_gamma)
 from .mxfp4 import e2m1_decode, e8m0_decode, mx_decode, attention_mxfp4_reference, mxfp4_bounds
+from .fp8_blocks import dequantise_blocks, v_ratios, attention_fp8_blockscaled_reference, fp8_blockscaled_bounds
 from . import roofline
 
 __all__ = [
@@ -61,4 +62,5 @@ __all__ = [
     "e4m3_decode", "dequantise", "attention_fp8_reference", "fp8_output_bound", "fp8_score_error_bound",
     "fp8_float32_bound", "summation_gamma",
     "e2m1_decode", "e8m0_decode", "mx_decode", "attention_mxfp4_reference", "mxfp4_bounds",
+    "dequantise_blocks", "v_ratios", "attention_fp8_blockscaled_reference", "fp8_blockscaled_bounds",
 ]

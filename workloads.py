@@ -139,3 +139,20 @@ def quantise_mxfp4(x, block=32):
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).to(torch.uint8).contiguous()
     scales = (X.squeeze(-1) + 127).to(torch.uint8).contiguous()
     return packed, scales
+
+
+def quantise_e4m3_blocks(x, block=128, amax=224.0):
+    """e4m3 codes of x [B,H,S,d] with one dequantisation factor per block of
+    `block` consecutive rows of each (batch, head) slice (the last block may
+    be shorter): each block is divided by its max|x| / amax (1 for an
+    all-zero block) and converted with torch's round-to-nearest
+    float8_e4m3fn.  Returns (uint8 codes, float32 factors [B,H,ceil(S/block)])."""
+    B, H, S, d = x.shape
+    nb = (S + block - 1) // block
+    xf = x.float()
+    pad = torch.zeros((B, H, nb * block - S, d), dtype=torch.float32)
+    blocks = torch.cat([xf, pad], dim=2).reshape(B, H, nb, block, d)
+    m = blocks.abs().amax(dim=(3, 4))
+    f = torch.where(m > 0, m / amax, torch.ones_like(m))
+    codes = (blocks / f[:, :, :, None, None]).reshape(B, H, nb * block, d)[:, :, :S]
+    return codes.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), f.contiguous()
