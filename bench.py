@@ -340,6 +340,18 @@ def main():
                     extra[f"{ww.name}-fp8-tau0"] = {
                         "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3", "tau": 0.0,
                         "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
+                # the same tensors with one factor per 128-row block of Q, K, V
+                from workloads import quantise_e4m3_blocks
+                (qb8, qbf), (kb8, kbf), (vb8, vbf) = (quantise_e4m3_blocks(t.cpu()) for t in (qq, kk, vv))
+                qb8, kb8, vb8, qbf, kbf, vbf = (t.to(dev) for t in (qb8, kb8, vb8, qbf, kbf, vbf))
+                ms = time_calls(lambda: fa.fa_fwd_fp8_blocks(qb8, kb8, vb8, qbf, kbf, vbf, oo, ll, causal=ww.causal,
+                                                             scale=ww.scale, tau=args.tau),
+                                max(10, args.steps), 3, args.warm_seconds / 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}-fp8-blocks"] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3, one factor per 128-row block",
+                    "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
+                del qb8, kb8, vb8, qbf, kbf, vbf
                 # MXFP4 Q and K (E8M0 scales per 32 dims), e4m3 V: S on the
                 # scaled fp4 products, P V in e4m3
                 from workloads import quantise_mxfp4

@@ -16,7 +16,8 @@ import os
 __all__ = [
     "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
     "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
-    "backward", "fa_bwd_noalloc", "fa_fwd_mxfp4", "forward_mxfp4", "LIB_PATH",
+    "backward", "fa_bwd_noalloc", "fa_fwd_mxfp4", "forward_mxfp4", "fa_fwd_fp8_blocks", "forward_fp8_blocks",
+    "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -50,6 +51,8 @@ def lib():
     L.fa_fwd_rescale_count.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
     L.fa_fwd_fp8.restype = i
+    L.fa_fwd_fp8_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
+    L.fa_fwd_fp8_blocks.restype = i
     L.fa_fwd_mxfp4.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, f, f, vp]
     L.fa_fwd_mxfp4.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, f, f, vp]
@@ -182,6 +185,35 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, q_descale=1.0, k_descale=1.0, v_descale=1.0, 
                           _stream(q8))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
+
+
+FA_FP8_SCALE_BLOCK = 128
+
+
+def fa_fwd_fp8_blocks(q8, k8, v8, q_factors, k_factors, v_factors, o, lse, causal=False, scale=None, tau=8.0):
+    """Enqueue the e4m3 forward with per-block factors on the current
+    stream; fills the bf16 o and the float32 lse in place.  q8, k8, v8 hold
+    e4m3 bytes; q_factors is a float32 CUDA tensor [B, H, ceil(Sq / 128)],
+    k_factors and v_factors [B, H, ceil(Sk / 128)]: the factor of each block
+    of 128 consecutive rows."""
+    B, H, Sq, d = q8.shape
+    Sk = k8.shape[2]
+    nq, nk = -(-Sq // FA_FP8_SCALE_BLOCK), -(-Sk // FA_FP8_SCALE_BLOCK)
+    _check_e4m3("q8", q8, (B, H, Sq, d))
+    _check_e4m3("k8", k8, (B, H, Sk, d))
+    _check_e4m3("v8", v8, (B, H, Sk, d))
+    _check_f32("q_factors", q_factors, (B, H, nq))
+    _check_f32("k_factors", k_factors, (B, H, nk))
+    _check_f32("v_factors", v_factors, (B, H, nk))
+    _check_bf16("o", o, (B, H, Sq, d))
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_fp8_blocks(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_factors), _ptr(k_factors), _ptr(v_factors),
+                                 _ptr(o), _ptr(lse), B, H, Sq, Sk, d, int(bool(causal)), float(scale), float(tau),
+                                 _stream(q8))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8_blocks")
 
 
 def _check_u8(name, t, shape):
@@ -336,6 +368,17 @@ def forward_fp8(q8, k8, v8, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
     fa_fwd_fp8(q8, k8, v8, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, tau=tau,
                head_descales=head_descales)
+    return o, lse
+
+
+def forward_fp8_blocks(q8, k8, v8, q_factors, k_factors, v_factors, causal=False, scale=None, tau=8.0):
+    """Returns (O bf16 [B,H,Sq,d], LSE float32 [B,H,Sq]) of the e4m3 forward
+    with per-block factors."""
+    import torch
+    B, H, Sq, d = q8.shape
+    o = torch.empty((B, H, Sq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8_blocks(q8, k8, v8, q_factors, k_factors, v_factors, o, lse, causal=causal, scale=scale, tau=tau)
     return o, lse
 
 

@@ -133,6 +133,35 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_fp8_blocks(const void* Q8, const void* K8, const void* V8, const float* q_factors,
+                            const float* k_factors, const float* v_factors, void* O, float* LSE, int B, int H,
+                            int Sq, int Sk, int d, int causal, float scale, float tau, void* stream) {
+  if (!Q8 || !K8 || !V8 || !q_factors || !k_factors || !v_factors || !O || !LSE) return FA_ERR_INVALID;
+  if (!aligned16(Q8) || !aligned16(K8) || !aligned16(V8) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_INVALID;
+  for (const float* f : {q_factors, k_factors, v_factors})
+    if (reinterpret_cast<uintptr_t>(f) % alignof(float) != 0) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (!(isfinite(scale * 1.4426950408889634f) && scale * 1.4426950408889634f >= FLT_MIN)) return FA_ERR_INVALID;
+  if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdFp8Args a;
+  a.q = Q8; a.k = K8; a.v = V8; a.o = O; a.lse = LSE;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.q_descale = a.k_descale = a.v_descale = 1.0f;
+  a.head_descales = nullptr;
+  a.q_blocks = q_factors; a.k_blocks = k_factors; a.v_blocks = v_factors;
+  a.tau = tau;
+  const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_mxfp4(const void* Q4, const void* Q_scales, const void* K4, const void* K_scales, const void* V8,
                         float v_descale, void* O, float* LSE, int B, int H, int Sq, int Sk, int d, int causal,
                         float scale, float tau, void* stream) {

@@ -70,6 +70,11 @@ struct Fwd8Params {
   float v_descale;
   const float* hd;   // null, or per-slice factors [3][BH] (q, k, v)
   float tau;
+  // BS: per-block factors [BH][nqb], [BH][nkb], [BH][nkb] (128-row blocks)
+  const float* qbs;
+  const float* kbs;
+  const float* vbs;
+  int nqb, nkb;
 };
 
 // the 16-byte chunk c of K tile row r sits at byte r * kD8 + 16 * (c ^ swz8(r)):
@@ -166,8 +171,16 @@ __device__ __forceinline__ void dma_tile4(__amdgpu_buffer_rsrc_t src, __amdgpu_b
 }
 
 // FP4QK: Q and K in MXFP4 (S^T on the scaled fp4 products), V and P in e4m3.
-template <bool CAUSAL, bool FP4QK = false>
+// BS: one dequantisation factor per 128-row block of Q, K and V: Q's folds
+// into the wave's score factor (a wave's 32 rows lie in one block), K's into
+// the tile's (a 128-key tile is one block); V's enters the exponent: the tile
+// rounds r P to e4m3, r = its V factor / the head's largest, sums P itself
+// for the row sum (the tile's partial sums times 1 / r), and the epilogue
+// multiplies O by the largest factor.
+template <bool CAUSAL, bool FP4QK = false, bool BS = false>
 __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
+  static_assert(!(FP4QK && BS), "block factors are for the e4m3 operands");
+  static_assert(kBN8 == kFp8ScaleBlock && kFp8ScaleBlock % kQW8 == 0, "a tile is one K / V block, a wave in one Q block");
   constexpr int kKB = kBN8 / 32;   // 32-key blocks of S^T per tile
   constexpr int kKC = kD8 / 64;    // 64-dim steps of S^T
   constexpr int kKS = kBN8 / 64;   // 64-key steps of P V
@@ -198,6 +211,31 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 
   const int q_wave_lo = qb * kBM8 + wave * kQW8;
   const int q_lane = q_wave_lo + r32;
+
+  // block factors: the wave's Q block into the score factor; the head's
+  // largest V factor (each lane takes every 64th block, then a wave max).
+  // Per tile the vector phase needs the tile's score factor and log2 r: lane
+  // l holds those of tile w0 + l of a 64-tile window (refilled every 64
+  // tiles), read per tile with readlane, so no tile waits on a memory load
+  // (a vector-memory wait would also wait for the tile loads in flight).
+  const float* kbs_head = BS ? p.kbs + (size_t)bh * p.nkb : nullptr;
+  const float* vbs_head = BS ? p.vbs + (size_t)bh * p.nkb : nullptr;
+  float inv_vmax = 1.0f, c_win = 0.0f, lr_win = 0.0f;
+  auto fill_window = [&](int w0) __attribute__((always_inline)) {
+    const int b = min(w0 + lane, p.nkb - 1);
+    c_win = s_log2 * kbs_head[b];
+    lr_win = __builtin_amdgcn_logf(vbs_head[b] * inv_vmax);
+  };
+  if constexpr (BS) {
+    s_log2 *= p.qbs[(size_t)bh * p.nqb + min(q_wave_lo / kFp8ScaleBlock, p.nqb - 1)];
+    float vmax = 0.0f;
+    for (int b = lane; b < p.nkb; b += 64) vmax = __builtin_fmaxf(vmax, vbs_head[b]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, off));
+    v_descale = vmax;
+    inv_vmax = 1.0f / vmax;
+    fill_window(0);
+  }
 
   // Q^T operand, k-step kc: lane holds Q[q_lane][64 kc + 32 g .. +31]
   i32x8 qf[kKC];
@@ -378,13 +416,30 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
       softmax_mask_prefix<kKB>(s, last - k0 - 4 * g);
     }
     const float mx = softmax_row_max<kKB>(s);
-    softmax_conditional_rescale(m_ref, mx * s_log2, p.tau, [&](float alpha) {
+    // the tile's score factor (BS: times its K block's factor)
+    float c_t = s_log2, log2_r = 0.0f;
+    if constexpr (BS) {
+      if ((t & 63) == 0 && t > 0) fill_window(t);
+      c_t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c_win), t & 63));
+      log2_r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lr_win), t & 63));
+    }
+    softmax_conditional_rescale(m_ref, mx * c_t, p.tau, [&](float alpha) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) l_part[c] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     });
-    softmax_exp_rowsum<kKB, 0>(s, s_log2, m_ref, l_part);
+    if constexpr (BS) {
+      // P' = r P = 2^(s c - (m_ref - log2 r)), r = V factor / the largest (<= 1);
+      // the partial sums go back by 2^-log2 r, the same factor P' carries
+      float l_tile[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      softmax_exp_rowsum<kKB, 0>(s, c_t, m_ref - log2_r, l_tile);
+      const float inv_r = __builtin_amdgcn_exp2f(-log2_r);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l_part[c] = __builtin_fmaf(l_tile[c], inv_r, l_part[c]);
+    } else {
+      softmax_exp_rowsum<kKB, 0>(s, c_t, m_ref, l_part);
+    }
     // P^T operand of 64-key step ks: bytes j = 0..31 are s[2 ks + j / 16][j % 16]
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
@@ -511,6 +566,17 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
   prm.v_descale = a.v_descale;
   prm.hd = a.head_descales;
   prm.tau = a.tau;
+  prm.qbs = a.q_blocks;
+  prm.kbs = a.k_blocks;
+  prm.vbs = a.v_blocks;
+  prm.nqb = (a.Sq + kFp8ScaleBlock - 1) / kFp8ScaleBlock;
+  prm.nkb = (a.Sk + kFp8ScaleBlock - 1) / kFp8ScaleBlock;
+  const bool bs = a.q_blocks != nullptr;
+  if (bs) {   // the block factors replace the per-tensor and per-slice ones
+    prm.s_log2 = a.scale * kLog2e;
+    prm.v_descale = 1.0f;
+    prm.hd = nullptr;
+  }
   const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
   auto run = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -519,6 +585,7 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, grid, dim3(kThreads8), kLds8, stream, prm);
     return hipGetLastError();
   };
+  if (bs) return a.causal ? run(fwd8_kernel<true, false, true>) : run(fwd8_kernel<false, false, true>);
   return a.causal ? run(fwd8_kernel<true>) : run(fwd8_kernel<false>);
 }
 
@@ -539,6 +606,8 @@ hipError_t launch_fwd_mxfp4(const FwdFp8Args& a, hipStream_t stream) {
   prm.v_descale = a.v_descale;
   prm.hd = nullptr;
   prm.tau = a.tau;
+  prm.qbs = prm.kbs = prm.vbs = nullptr;
+  prm.nqb = prm.nkb = 0;
   const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
   auto run = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -47,7 +47,14 @@ struct FwdFp8Args {
   const float* head_descales;   // null or [3][B*H] on the device
   const void* q_scales = nullptr;   // MXFP4: E8M0 scales [B*H][Sq][4], [B*H][Sk][4]
   const void* k_scales = nullptr;
+  // per-block factors (one per kFp8ScaleBlock rows of a (batch, head) slice):
+  // float32 [B*H][ceil(Sq / 128)], [B*H][ceil(Sk / 128)] twice; null for the
+  // per-tensor form (then q_descale, k_descale, v_descale, head_descales apply)
+  const float* q_blocks = nullptr;
+  const float* k_blocks = nullptr;
+  const float* v_blocks = nullptr;
 };
+constexpr int kFp8ScaleBlock = 128;
 hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream);
 // MXFP4 Q, K (E2M1 elements, d/2 bytes per row; E8M0 scales per 32 dims),
 // e4m3 V: q_descale and k_descale unused, head_descales null

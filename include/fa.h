@@ -116,6 +116,30 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
                      float v_descale, const float* head_descales, void* O, float* LSE, int B, int H, int Sq,
                      int Sk, int d, int causal, float scale, float tau, void* stream);
 
+/* Forward with e4m3 (OCP e4m3fn) operands and one dequantisation factor per
+ * block of FA_FP8_SCALE_BLOCK = 128 consecutive rows of each (batch, head)
+ * slice: the finer of the two scale forms the FlashAttention-4 summary's
+ * precision discussion leaves open for FP8 operands.  Q8, K8, V8 are e4m3
+ * bytes as for fa_fwd_fp8; q_factors is a float32 device array
+ * [B][H][ceil(Sq / 128)], k_factors and v_factors [B][H][ceil(Sk / 128)]
+ * (caller-owned, read by the kernel: finite and > 0, which the library
+ * cannot check before the launch; other values give non-finite outputs).
+ * The attention is computed on Q[b,h,i] = q_factors[b,h,i / 128] * Q8[b,h,i]
+ * (K, V likewise).  Scores accumulate in float32 and take the Q and K block
+ * factors as one score factor per 32-row wavefront and 128-key tile; the
+ * unnormalised probabilities are rounded to e4m3 as r P, r = the key block's
+ * V factor / the head's largest V factor (<= 1), before P V, and O is
+ * multiplied by that largest factor; the row sum and LSE use the float32 P.
+ * O is bf16 [B,H,Sq,d], LSE float32 [B,H,Sq].
+ *   0 <= tau <= 8; d = 128 only (else FA_ERR_UNSUPPORTED); causal requires
+ *   Sq = Sk; 16-byte aligned Q8, K8, V8, O, LSE; 4-byte aligned factors;
+ *   other arguments and errors as for fa_fwd.
+ * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
+#define FA_FP8_SCALE_BLOCK 128
+fa_status fa_fwd_fp8_blocks(const void* Q8, const void* K8, const void* V8, const float* q_factors,
+                            const float* k_factors, const float* v_factors, void* O, float* LSE, int B, int H,
+                            int Sq, int Sk, int d, int causal, float scale, float tau, void* stream);
+
 /* Forward with MXFP4 queries and keys and e4m3 values: the FP4 operand
  * experiment of the lecture notes "How FlashAttention 4 Works" (FP4 among
  * Blackwell's new formats, experimental in their map of which attention

@@ -207,3 +207,23 @@ def test_fwd_mxfp4_rejects_before_any_launch(L):
     assert call(causal=2) == fa.FA_ERR_INVALID
     assert call(d=64) == fa.FA_ERR_UNSUPPORTED
     assert call(causal=1, Sk=32) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fwd_fp8_blocks_rejects_before_any_launch(L):
+    vp = ctypes.c_void_p
+
+    def call(q=FAKE, k=FAKE, v=FAKE, qf=FAKE, kf=FAKE, vf=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Sq=16, Sk=16, d=128,
+             causal=0, scale=0.125, tau=8.0):
+        return L.fa_fwd_fp8_blocks(vp(q), vp(k), vp(v), vp(qf), vp(kf), vp(vf), vp(o), vp(lse), B, H, Sq, Sk, d,
+                                   causal, scale, tau, vp(0))
+    assert call(vf=0) == fa.FA_ERR_INVALID
+    assert call(qf=FAKE + 2) == fa.FA_ERR_INVALID          # factors must be 4-byte aligned
+    assert call(v=FAKE + 8) == fa.FA_ERR_INVALID
+    assert call(lse=0) == fa.FA_ERR_INVALID
+    assert call(tau=8.5) == fa.FA_ERR_INVALID
+    assert call(scale=float("nan")) == fa.FA_ERR_INVALID
+    assert call(scale=1e-40) == fa.FA_ERR_INVALID
+    assert call(B=0) == fa.FA_ERR_INVALID
+    assert call(causal=3) == fa.FA_ERR_INVALID
+    assert call(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=1, Sk=48) == fa.FA_ERR_UNSUPPORTED

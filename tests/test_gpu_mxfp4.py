@@ -50,7 +50,7 @@ def check(o, lse, O, L, bound, score_bound, what):
     err = np.abs(o - O)
     allowed = bound + 2.0 ** -8 * np.abs(O)
     lse_err = np.maximum(np.abs(lse - L) - score_bound, 0.0) / np.maximum(1.0, np.abs(L))
-    stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), worst_ratio=float((err / allowed).max()),
+    stats = dict(o_max=float(err.max()), o_mean=float(err.mean()), worst_ratio=float(np.where(allowed > 0, err / np.where(allowed > 0, allowed, 1.0), 0.0).max()),
                  lse_rel=float(lse_err.max()))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
     assert np.all(err <= allowed), (what, stats)
