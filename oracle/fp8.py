@@ -159,22 +159,25 @@ def summation_gamma(n, lam=10.0):
     return np.minimum(worst, prob)
 
 
-def float32_bound_of(q, k, v, scale, causal=False, shift_max=0.0, extra_roundings=0):
+def float32_bound_of(q, k, v, scale, causal=False, shift_max=None, extra_roundings=0):
     """fp8_float32_bound on dequantised float arrays q, k, v.  shift_max
-    ([B,H] or scalar, default 0): the largest |log2 r| of a per-key factor r
-    the kernel folds into the exponent (its one rounding adds u |log2 r| to a
-    score's error); extra_roundings: further roundings per term of the row
-    sum or per output element beyond the 16 counted here."""
+    ([B,H] or scalar, default none): the largest |log2 r| of a per-key factor
+    r the kernel folds into the exponent: r (one rounding, u relative) and its
+    log2 (within an ulp, 2 u |log2 r|) add 2 u (|log2 r| + 1) to a score's
+    error; extra_roundings: further roundings per term of the row sum or per
+    output element beyond the 16 counted here."""
     p = attention_probs(q, k, scale, causal)
     rel = np.einsum("bhij,bhjc->bhic", p, np.abs(_f64(v)))        # sum_j p_j |v_j|
     Sq, Sk = p.shape[-2], p.shape[-1]
     vis = np.tril(np.ones((Sq, Sk), dtype=bool)) if causal else np.ones((Sq, Sk), dtype=bool)
     s_abs = np.abs(scale * np.einsum("bhic,bhjc->bhij", _f64(q), _f64(k)))
     smax = np.where(vis, s_abs, 0.0).max(axis=-1)
-    shift = np.asarray(shift_max, dtype=np.float64)
-    if shift.ndim == 2:
-        shift = shift[:, :, None]
-    eps = score_error_bound_of(q, k, scale, causal) + 8.0 * U32 * smax + 2.0 * U32 * shift
+    eps = score_error_bound_of(q, k, scale, causal) + 8.0 * U32 * smax
+    if shift_max is not None:
+        shift = np.asarray(shift_max, dtype=np.float64)
+        if shift.ndim == 2:
+            shift = shift[:, :, None]
+        eps = eps + 2.0 * U32 * (shift + 1.0)
     n = vis.sum(axis=-1).astype(np.float64)                          # [Sq]
     factor = np.expm1(2.0 * eps) + 2.0 * summation_gamma(n) + (16.0 + extra_roundings) * U32
     return factor[..., None] * rel

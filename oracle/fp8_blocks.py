@@ -25,8 +25,8 @@ the unrounded P_j.  Per output element the rounding then moves O by at most
 exact weights, l_max = sum_j exp(s_j - max s) <= l).  With all factors equal,
 r_j = 1 and the bound is that of ``fp8_output_bound``.  The float32 arithmetic
 adds ``float32_bound_of`` on the dequantised tensors, with the exponent shift
-log2 r_j (one more rounding per score) and two more roundings per row-sum
-term (the tile's partial sum is multiplied by 1 / r) counted in.
+log2 r_j (r_j and its log2 each rounded once) and two more roundings per
+row-sum term (the tile's partial sum is multiplied by 2^-log2 r) counted in.
 
 Pins (tests/test_oracle_fp8_blocks.py): block dequantisation against a scalar
 loop (ragged last block included) and, with equal factors, against the
