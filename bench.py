@@ -399,6 +399,18 @@ def main():
                 counts["wave_tile_steps_after_first"] = steps * ww.B * ww.H
                 extra[f"{ww.name}-rescale_events"] = counts
             if wid == 4:
+                # the d = 64 rescale-stress workload on e4m3 inputs (per-tensor factors)
+                from workloads import quantise_e4m3
+                (q8, qs), (k8, ks), (v8, vs) = (quantise_e4m3(t.cpu()) for t in (qq, kk, vv))
+                q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+                ms = time_calls(lambda: fa.fa_fwd_fp8(q8, k8, v8, oo, ll, qs, ks, vs, causal=ww.causal,
+                                                      scale=ww.scale, tau=args.tau),
+                                max(10, args.steps), 3, args.warm_seconds / 3)
+                tf = ww.flops("fwd") / (ms * 1e-3) / 1e12
+                extra[f"{ww.name}-fp8"] = {
+                    "ms": round(ms, 5), "tflops": round(tf, 2), "dtype": "e4m3",
+                    "pct_peak_fp8": round(100 * tf / PEAK_FP8_TFLOPS, 2), "peak_tflops": PEAK_FP8_TFLOPS}
+                del q8, k8, v8
                 # ablation of the conditional rescale: tau = 0 corrects the
                 # output on every increase of a row max (the eager online softmax)
                 ms = time_calls(lambda: fa.fa_fwd(qq, kk, vv, oo, ll, causal=ww.causal, scale=ww.scale,

@@ -117,13 +117,13 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
   if (!(isfinite(score_factor) && score_factor >= FLT_MIN)) return FA_ERR_INVALID;
   if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
-  if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
   if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
   if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdFp8Args a;
   a.q = Q8; a.k = K8; a.v = V8; a.o = O; a.lse = LSE;
-  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.causal = causal != 0;
   a.scale = scale;
   a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
@@ -145,13 +145,13 @@ fa_status fa_fwd_fp8_blocks(const void* Q8, const void* K8, const void* V8, cons
   if (!(isfinite(scale * 1.4426950408889634f) && scale * 1.4426950408889634f >= FLT_MIN)) return FA_ERR_INVALID;
   if (!(isfinite(tau) && tau >= 0.0f && tau <= 8.0f)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
-  if (d != FA_D_LARGE) return FA_ERR_UNSUPPORTED;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
   if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
   if (!head_addressable(Sq, Sk, d)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdFp8Args a;
   a.q = Q8; a.k = K8; a.v = V8; a.o = O; a.lse = LSE;
-  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.causal = causal != 0;
   a.scale = scale;
   a.q_descale = a.k_descale = a.v_descale = 1.0f;

@@ -88,6 +88,17 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 // and 3 select the chunk pair, so the four rows of a parity cover the 8 bank
 // slots of their half once (swz8 maps them to two pairs: a 2-way conflict)
 __device__ __forceinline__ int swzv(int r) { return (r & 2) | ((r >> 1) & 4); }
+// d = 64: 64-byte rows, four to a 256-byte bank line.  K chunk c of row r at
+// c ^ swz64(r): the four rows of a read pass that share a line (r, r + 4,
+// r + 8, r + 12) take distinct chunks.  V at c ^ swzv64(r): a transposed
+// read pass touches rows r0 + i and r0 + 8 + i (i < 4) that share a line,
+// two chunks each, so row bit 3 picks the chunk pair.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swzv64(int r) { return (r >> 2) & 2; }
+template <int D8>
+__device__ __forceinline__ int k_swz(int r) { return D8 == 128 ? swz8(r) : swz64(r); }
+template <int D8>
+__device__ __forceinline__ int v_swz(int r) { return D8 == 128 ? swzv(r) : swzv64(r); }
 
 // e4m3 x e4m3 products written out as single instructions (the compiler
 // moves its own form of this product past barriers to the first use of the
@@ -104,6 +115,9 @@ __device__ __forceinline__ void mfma8_init(f32x16& d, const i32x8& a, const i32x
 }
 __device__ __forceinline__ void drain8(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void drain8(f32x16& a, f32x16& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
 }
 
 // MXFP4 x MXFP4 products (E2M1 elements, 4 VGPRs per operand) with E8M0
@@ -143,18 +157,20 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t row_scales, int g) {
 // k-slot j of lane group g (0, 1) -> key of the 64-key step
 __device__ __forceinline__ int slot_key(int g, int j) { return 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * g + (j % 4); }
 
-// a tile of 128 rows, memory-to-LDS with the chunk permutation (swz8 for K,
-// swzv for V): one 16-byte load per lane covers 8 whole rows; a wave issues
-// 2 of the 16
-template <bool V_TILE>
+// a tile of 128 rows of D8 bytes, memory-to-LDS with the chunk permutation
+// (K or V): one 16-byte load per lane covers 1024 / D8 whole rows (8 at
+// d = 128, 16 at d = 64); the waves share the tile's loads
+template <int D8, bool V_TILE>
 __device__ __forceinline__ void dma_tile8(__amdgpu_buffer_rsrc_t src, int row0, char* tile, int wave, int lane) {
+  constexpr int kLanesPerRow = D8 / 16, kRowsPerLoad = 64 / kLanesPerRow;
+  static_assert(kBN8 % (kRowsPerLoad * kWaves8) == 0, "the waves share the loads evenly");
 #pragma unroll
-  for (int i = 0; i < kBN8 / 8 / kWaves8; ++i) {
+  for (int i = 0; i < kBN8 / kRowsPerLoad / kWaves8; ++i) {
     const int blk = i * kWaves8 + wave;   // wave-uniform
-    const int row = blk * 8 + lane / 8;
-    const int sw = V_TILE ? swzv(row) : swz8(row);
-    const unsigned off = (unsigned)(row0 + row) * kD8 + 16 * ((lane % 8) ^ sw);
-    lds_dma16(src, off, tile + blk * 8 * kD8);
+    const int row = blk * kRowsPerLoad + lane / kLanesPerRow;
+    const int sw = V_TILE ? v_swz<D8>(row) : k_swz<D8>(row);
+    const unsigned off = (unsigned)(row0 + row) * D8 + 16 * ((lane % kLanesPerRow) ^ sw);
+    lds_dma16(src, off, tile + blk * kRowsPerLoad * D8);
   }
 }
 
@@ -177,14 +193,16 @@ __device__ __forceinline__ void dma_tile4(__amdgpu_buffer_rsrc_t src, __amdgpu_b
 // rounds r P to e4m3, r = its V factor / the head's largest, sums P itself
 // for the row sum (the tile's partial sums times 1 / r), and the epilogue
 // multiplies O by the largest factor.
-template <bool CAUSAL, bool FP4QK = false, bool BS = false>
+template <bool CAUSAL, bool FP4QK = false, bool BS = false, int D8 = 128>
 __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   static_assert(!(FP4QK && BS), "block factors are for the e4m3 operands");
+  static_assert(D8 == 128 || (D8 == 64 && !FP4QK), "head dimension 128, or 64 with e4m3 operands");
+  constexpr int kTileD = kBN8 * D8;   // bytes of an e4m3 K or V tile
   static_assert(kBN8 == kFp8ScaleBlock && kFp8ScaleBlock % kQW8 == 0, "a tile is one K / V block, a wave in one Q block");
   constexpr int kKB = kBN8 / 32;   // 32-key blocks of S^T per tile
-  constexpr int kKC = kD8 / 64;    // 64-dim steps of S^T
+  constexpr int kKC = D8 / 64;    // 64-dim steps of S^T
   constexpr int kKS = kBN8 / 64;   // 64-key steps of P V
-  constexpr int kDB = kD8 / 32;    // 32-dim blocks of O^T
+  constexpr int kDB = D8 / 32;    // 32-dim blocks of O^T
   constexpr int kNV = kKS * kDB;   // P V products per tile
   constexpr int kNK = kKB * kKC;   // K Q^T products per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -204,10 +222,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
     v_descale *= p.hd[2 * p.BH + bh];
   }
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
-  constexpr int kRowQK = FP4QK ? kRow4 : kD8;   // bytes per Q / K row
+  constexpr int kRowQK = FP4QK ? kRow4 : D8;   // bytes per Q / K row
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * kRowQK, (unsigned)p.Sq * kRowQK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * kRowQK, (unsigned)p.Sk * kRowQK);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * kD8, (unsigned)p.Sk * kD8);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D8, (unsigned)p.Sk * D8);
 
   const int q_wave_lo = qb * kBM8 + wave * kQW8;
   const int q_lane = q_wave_lo + r32;
@@ -255,14 +273,14 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   } else {
 #pragma unroll
     for (int kc = 0; kc < kKC; ++kc) {
-      qf[kc].lo = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g));
-      qf[kc].hi = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * kD8 + 64 * kc + 32 * g + 16));
+      qf[kc].lo = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * D8 + 64 * kc + 32 * g));
+      qf[kc].hi = __builtin_bit_cast(i32x4, load16(rq, (unsigned)q_lane * D8 + 64 * kc + 32 * g + 16));
     }
   }
 
   // K operand addresses: row 32 kb + r32 has the chunk permutation of r32
-  const int k_sw = swz8(r32);
-  const int k_row = r32 * kD8;
+  const int k_sw = k_swz<D8>(r32);
+  const int k_row = r32 * D8;
   // V^T operand addresses: read q of a 64-key step; this lane, as a source
   // lane of its 16-lane group, addresses the key of k-slot 8 q + m (m = (lane
   // % 16) / 2) and the dims 32 db + 16 half + 8 par .. +7 (half = group of
@@ -279,15 +297,15 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = slot_key(g, 8 * q + m8);
-    const int sw = swzv(row);
+    const int sw = v_swz<D8>(row);
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
-      v_off[q][db] = row * kD8 + 8 * par + 16 * (half ^ (sw & 1)) + ((32 * db) ^ (32 * (sw >> 1)));
+      v_off[q][db] = row * D8 + 8 * par + 16 * (half ^ (sw & 1)) + ((32 * db) ^ (32 * (sw >> 1)));
   }
   // K operand reads: 16-byte chunk 4 kc + 2 g + h of row r32, swizzled
-  int k_off[2][2];
+  int k_off[kKC][2];
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
+  for (int kc = 0; kc < kKC; ++kc)
 #pragma unroll
     for (int h = 0; h < 2; ++h) k_off[kc][h] = k_row + 16 * ((4 * kc + 2 * g + h) ^ k_sw);
 
@@ -308,10 +326,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
 
   // LDS ring: K stages 0, 1 then V stages 0, 1 (MXFP4 K stages are half a
   // tile plus the scale dwords)
-  constexpr int kStageK = FP4QK ? kStageK4 : kTile8;
+  constexpr int kStageK = FP4QK ? kStageK4 : kTileD;
   auto k_stage = [&](int u) __attribute__((always_inline)) -> char* { return smem + (u & 1) * kStageK; };
   auto v_stage = [&](int u) __attribute__((always_inline)) -> char* {
-    return smem + 2 * kStageK + (u & 1) * kTile8;
+    return smem + 2 * kStageK + (u & 1) * kTileD;
   };
   // MXFP4 K operand: row 32 kb + r32, bytes 32 kc + 16 g .. +15 (chunk 2 kc + g)
   int k4_off[2];
@@ -333,7 +351,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
         i32x8 r;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const char* a = vst + ks * 64 * kD8 + v_off[q][db];
+          const char* a = vst + ks * 64 * D8 + v_off[q][db];
           const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) i32x2*)(lds_addr(a)));
           r[2 * q] = t[0];
@@ -348,7 +366,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
         // 16 bytes (32 elements) per lane; the upper half of the ring entry is unused
         r.lo = *reinterpret_cast<const i32x4*>(kst + kb * 32 * kRow4 + k4_off[kc]);
       } else {
-        const char* row = kst + kb * 32 * kD8;
+        const char* row = kst + kb * 32 * D8;
         r.lo = *reinterpret_cast<const i32x4*>(row + k_off[kc][0]);
         r.hi = *reinterpret_cast<const i32x4*>(row + k_off[kc][1]);
       }
@@ -387,7 +405,10 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (PV) drain8(o[0], o[1], o[2], o[3]);
+    if constexpr (PV) {
+      if constexpr (kDB == 4) drain8(o[0], o[1], o[2], o[3]);
+      else drain8(o[0], o[1]);
+    }
     if (SK) drain8(s[0], s[1], s[2], s[3]);
   };
   auto matrix_stream = [&](int uk, int uv, auto with_pv, auto with_s) __attribute__((always_inline)) {
@@ -460,9 +481,9 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   auto fetch = [&](int u) __attribute__((always_inline)) {
     if (u < n) {
       if constexpr (FP4QK) dma_tile4(rk, rks, u * kBN8, k_stage(u), wave, lane);
-      else dma_tile8<false>(rk, u * kBN8, k_stage(u), wave, lane);
+      else dma_tile8<D8, false>(rk, u * kBN8, k_stage(u), wave, lane);
     }
-    if (u >= 1 && u <= n) dma_tile8<true>(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
+    if (u >= 1 && u <= n) dma_tile8<D8, true>(rv, (u - 1) * kBN8, v_stage(u - 1), wave, lane);
   };
   auto commit = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto barrier = [&]() __attribute__((always_inline)) {
@@ -544,7 +565,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   // ---- epilogue: O = v_descale O / l as bf16 rows, LSE = (m_ref + log2 l) ln 2
   const float l = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   const float inv_l = l > 0.0f ? v_descale / l : 0.0f;
-  RowStore<kD8>::store(smem + wave * RowStore<kD8>::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * kD8, q_wave_lo,
+  RowStore<D8>::store(smem + wave * RowStore<D8>::kBytes, o, inv_l, p.o + (size_t)bh * p.Sq * D8, q_wave_lo,
                        p.Sq, lane);
   if (q_lane < p.Sq && g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = (m_ref + __builtin_log2f(l)) * kLn2;
 }
@@ -572,6 +593,7 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
   prm.nqb = (a.Sq + kFp8ScaleBlock - 1) / kFp8ScaleBlock;
   prm.nkb = (a.Sk + kFp8ScaleBlock - 1) / kFp8ScaleBlock;
   const bool bs = a.q_blocks != nullptr;
+  const bool d64 = a.d == 64;
   if (bs) {   // the block factors replace the per-tensor and per-slice ones
     prm.s_log2 = a.scale * kLog2e;
     prm.v_descale = 1.0f;
@@ -585,6 +607,10 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, grid, dim3(kThreads8), kLds8, stream, prm);
     return hipGetLastError();
   };
+  if (d64) {
+    if (bs) return a.causal ? run(fwd8_kernel<true, false, true, 64>) : run(fwd8_kernel<false, false, true, 64>);
+    return a.causal ? run(fwd8_kernel<true, false, false, 64>) : run(fwd8_kernel<false, false, false, 64>);
+  }
   if (bs) return a.causal ? run(fwd8_kernel<true, false, true>) : run(fwd8_kernel<false, false, true>);
   return a.causal ? run(fwd8_kernel<true>) : run(fwd8_kernel<false>);
 }

@@ -42,6 +42,7 @@ struct FwdFp8Args {
   void* o;
   float* lse;
   int B, H, Sq, Sk;
+  int d = 128;   // 128, or 64 for the e4m3 forwards
   bool causal;
   float scale, q_descale, k_descale, v_descale, tau;
   const float* head_descales;   // null or [3][B*H] on the device

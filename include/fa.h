@@ -109,7 +109,7 @@ fa_status fa_fwd_rescale_count(const void* Q, const void* K, const void* V, void
  * the row sum and LSE use the float32 P.  O is bf16 [B,H,Sq,d], LSE float32
  * [B,H,Sq] (natural log, exact up to float32 rounding of the scores).
  *   0 <= tau <= 8 (P must stay below e4m3's largest value, 448);
- *   d = 128 only (else FA_ERR_UNSUPPORTED); causal requires Sq = Sk; other
+ *   d = 64 or 128 (else FA_ERR_UNSUPPORTED); causal requires Sq = Sk; other
  *   arguments and errors as for fa_fwd.  16-byte aligned device pointers.
  * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_descale, float k_descale,
@@ -131,7 +131,7 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* V8, float q_des
  * V factor / the head's largest V factor (<= 1), before P V, and O is
  * multiplied by that largest factor; the row sum and LSE use the float32 P.
  * O is bf16 [B,H,Sq,d], LSE float32 [B,H,Sq].
- *   0 <= tau <= 8; d = 128 only (else FA_ERR_UNSUPPORTED); causal requires
+ *   0 <= tau <= 8; d = 64 or 128 (else FA_ERR_UNSUPPORTED); causal requires
  *   Sq = Sk; 16-byte aligned Q8, K8, V8, O, LSE; 4-byte aligned factors;
  *   other arguments and errors as for fa_fwd.
  * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */

@@ -72,8 +72,8 @@ def _fwd8(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, h
     (dict(v=0), fa.FA_ERR_INVALID), (dict(k=FAKE + 8), fa.FA_ERR_INVALID), (dict(H=0), fa.FA_ERR_INVALID),
     (dict(qs=0.0), fa.FA_ERR_INVALID), (dict(vs=-1.0), fa.FA_ERR_INVALID), (dict(ks=float("inf")), fa.FA_ERR_INVALID),
     (dict(tau=8.5), fa.FA_ERR_INVALID), (dict(scale=-1.0), fa.FA_ERR_INVALID), (dict(causal=3), fa.FA_ERR_INVALID),
-    (dict(d=64), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=8), fa.FA_ERR_UNSUPPORTED),
-    (dict(hd=FAKE + 2), fa.FA_ERR_INVALID), (dict(hd=FAKE + 4, d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(causal=1, Sq=16, Sk=8), fa.FA_ERR_UNSUPPORTED),
+    (dict(hd=FAKE + 2), fa.FA_ERR_INVALID), (dict(hd=FAKE + 4, d=32), fa.FA_ERR_UNSUPPORTED),
     # each factor valid on its own, their product (folded into one float
     # score factor) overflows or underflows
     (dict(qs=1e30, ks=1e30), fa.FA_ERR_INVALID), (dict(qs=1e-30, ks=1e-20), fa.FA_ERR_INVALID),
@@ -225,5 +225,5 @@ def test_fwd_fp8_blocks_rejects_before_any_launch(L):
     assert call(scale=1e-40) == fa.FA_ERR_INVALID
     assert call(B=0) == fa.FA_ERR_INVALID
     assert call(causal=3) == fa.FA_ERR_INVALID
-    assert call(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
     assert call(causal=1, Sk=48) == fa.FA_ERR_UNSUPPORTED

@@ -268,3 +268,50 @@ def test_fp8_run_to_run_bitwise():
     a = run(q8, k8, v8, qs, ks, vs, True)
     b = run(q8, k8, v8, qs, ks, vs, True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- d = 64 (64-byte rows: one 64-dim step for S^T, two 32-dim output blocks)
+@pytest.mark.parametrize("Sq,Sk,causal", [(1, 1, False), (17, 17, True), (128, 128, False), (257, 257, True),
+                                          (200, 333, False), (384, 384, True)])
+def test_fp8_d64_small_shapes_every_element(Sq, Sk, causal):
+    say(f"fp8 fwd d64 B2 H3 Sq={Sq} Sk={Sk} causal={causal}")
+    d = 64
+    q8, k8, v8, qs, ks, vs = quantised(2, 3, Sq, Sk, d, seed=Sq * 11 + Sk)
+    o, lse = run(q8, k8, v8, qs, ks, vs, causal)
+    scale = 1 / math.sqrt(d)
+    O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, causal)
+    bound = bounds(q8, k8, v8, qs, ks, vs, scale, causal)
+    sb = fp8_score_error_bound(q8, k8, qs, ks, scale, causal)
+    say(check(o, lse, O, L, bound, f"d64 {Sq}x{Sk} c{causal}", sb))
+
+
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_fp8_d64_many_heads_and_key_ramp_every_element(tau):
+    """64 heads at S = 1000 (ragged last tile), and the rescale-stress key
+    ramp at S = 1536, at d = 64."""
+    d = 64
+    scale = 1 / math.sqrt(d)
+    for (B, H, S, ramp, seed) in [(1, 64, 1000, 0.0, 71), (1, 4, 1536, 6.0, 73)]:
+        say(f"fp8 fwd d64 B{B} H{H} S{S} ramp={ramp} tau={tau}")
+        q8, k8, v8, qs, ks, vs = quantised(B, H, S, S, d, seed=seed, key_ramp=ramp)
+        o, lse = run(q8, k8, v8, qs, ks, vs, True, tau)
+        O, L = attention_fp8_reference(q8, k8, v8, qs, ks, vs, scale, True)
+        bound = bounds(q8, k8, v8, qs, ks, vs, scale, True)
+        sb = fp8_score_error_bound(q8, k8, qs, ks, scale, True)
+        say(check(o, lse, O, L, bound, f"d64 H{H} S{S} ramp={ramp} tau={tau}", sb))
+
+
+def test_fp8_d64_causal_prefix_independence_and_run_to_run_bitwise():
+    say("fp8 fwd d64 causal prefix independence, run to run")
+    S, i, d = 320, 150, 64
+    q8, k8, v8, qs, ks, vs = quantised(1, 2, S, S, d, seed=75)
+    o1, l1 = run(q8, k8, v8, qs, ks, vs, True)
+    o1b, l1b = run(q8, k8, v8, qs, ks, vs, True)
+    assert np.array_equal(o1, o1b) and np.array_equal(l1, l1b)
+    k2, v2 = k8.clone(), v8.clone()
+    k2[:, :, i + 1:] = 0x7E
+    v2[:, :, i + 1:] = 0xFE
+    o2, l2 = run(q8, k2, v2, qs, ks, vs, True)
+    assert np.array_equal(o1[:, :, :i + 1], o2[:, :, :i + 1])
+    assert np.array_equal(l1[:, :, :i + 1], l2[:, :, :i + 1])
+    assert not np.array_equal(o1[:, :, i + 1:], o2[:, :, i + 1:])

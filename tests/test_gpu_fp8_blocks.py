@@ -26,11 +26,11 @@ def say(*a):
     sys.stdout.flush()
 
 
-def quantised(B, H, Sq, Sk, seed, key_ramp=0.0, spread=0):
+def quantised(B, H, Sq, Sk, seed, key_ramp=0.0, spread=0, d=D):
     """Seeded bf16 inputs in float32; spread > 0 scales each 128-row block by
     2^u, u uniform in -spread .. spread (V's blocks then span a wide range of
     ratios to the largest), before block quantisation."""
-    q, k, v = (t.float() for t in make_inputs(B, H, Sq, Sk, D, seed=seed, key_ramp=key_ramp))
+    q, k, v = (t.float() for t in make_inputs(B, H, Sq, Sk, d, seed=seed, key_ramp=key_ramp))
     if spread:
         g = torch.Generator().manual_seed(seed + 1)
         for t in (q, k, v):
@@ -63,7 +63,7 @@ def check(o, lse, O, L, bound, score_bound, what):
 def full_check(inputs, causal, tau, what):
     q8, qf, k8, kf, v8, vf = inputs
     o, lse = run(q8, qf, k8, kf, v8, vf, causal, tau)
-    scale = 1 / math.sqrt(D)
+    scale = 1 / math.sqrt(q8.shape[-1])
     O, L = attention_fp8_blockscaled_reference(q8, k8, v8, qf, kf, vf, scale, causal)
     bound, sb = fp8_blockscaled_bounds(q8, k8, v8, qf, kf, vf, scale, causal)
     return check(o, lse, O, L, bound, sb, what)
@@ -149,3 +149,11 @@ def test_fp8_blocks_causal_prefix_independence_and_run_to_run_bitwise():
     assert np.array_equal(o1[:, :, :i + 1], o2[:, :, :i + 1])
     assert np.array_equal(l1[:, :, :i + 1], l2[:, :, :i + 1])
     assert not np.array_equal(o1[:, :, i + 1:], o2[:, :, i + 1:])
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,tau", [(17, 17, True, 8.0), (200, 333, False, 8.0), (384, 384, True, 0.0),
+                                              (1000, 1000, True, 8.0)])
+def test_fp8_blocks_d64_every_element(Sq, Sk, causal, tau):
+    say(f"fp8 blocks d64 B2 H3 Sq={Sq} Sk={Sk} causal={causal} tau={tau}")
+    say(full_check(quantised(2, 3, Sq, Sk, seed=Sq * 13 + Sk, spread=3, d=64), causal, tau,
+                   f"d64 {Sq}x{Sk} c{causal} tau={tau}"))

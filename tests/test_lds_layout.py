@@ -80,3 +80,43 @@ def test_k_reads_conflict_free():
         for c in range(4):
             addrs = [(32 * kb + r) * 64 + 16 * (c ^ swz4(r)) for r in range(32)]
             assert worst_conflict(addrs, 16, 16) == 1
+
+
+# ---- e4m3 tiles at d = 64: 64-byte rows (4 rows per 256-byte bank line)
+def swz64(r):
+    return (r >> 2) & 3
+
+
+def swzv64(r):
+    return (r >> 2) & 2
+
+
+def v64_read_addrs(sw, ks, q, db):
+    out = []
+    for lane in range(64):
+        g, par, m8, half = lane >> 5, lane & 1, (lane & 15) >> 1, (lane >> 4) & 1
+        row = slot_key(g, 8 * q + m8)
+        s = sw(row)
+        out.append(ks * 64 * 64 + row * 64 + 8 * par + 16 * (half ^ (s & 1)) + ((32 * db) ^ (32 * (s >> 1))))
+    return out
+
+
+def test_d64_v_reads_address_their_logical_chunks_and_are_conflict_free():
+    for ks in range(2):
+        for q in range(4):
+            for db in range(2):
+                addrs = v64_read_addrs(swzv64, ks, q, db)
+                for lane, a in enumerate(addrs):
+                    g, par, m8, half = lane >> 5, lane & 1, (lane & 15) >> 1, (lane >> 4) & 1
+                    row = slot_key(g, 8 * q + m8)
+                    assert a // 64 == ks * 64 + row
+                    assert ((a % 64) // 16) ^ swzv64(row) == 2 * db + half and (a % 16) // 8 == par
+                assert worst_conflict(addrs, 8, 32) == 1
+
+
+def test_d64_k_reads_conflict_free():
+    # lane (r32, g) reads chunks 2 g, 2 g + 1 of row r32 of a 32-key block
+    for kb in range(4):
+        for c in range(4):
+            addrs = [(32 * kb + r) * 64 + 16 * (c ^ swz64(r)) for r in range(32)]
+            assert worst_conflict(addrs, 16, 16) == 1
