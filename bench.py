@@ -68,6 +68,8 @@ def parse():
                    help="with --reps and --fwd-only: run the e4m3 forward on the quantised workload")
     p.add_argument("--mxfp4", action="store_true",
                    help="with --reps and --fwd-only: run the MXFP4 forward (MXFP4 Q, K; e4m3 V)")
+    p.add_argument("--fp8-blocks", action="store_true",
+                   help="with --reps and --fwd-only: run the e4m3 forward with one factor per 128-row block")
     return p.parse_args()
 
 
@@ -214,6 +216,16 @@ def main():
 
             def fwd():
                 fa.fa_fwd_fp8(q8, k8, v8, o, lse, qs, ks, vs, causal=w.causal, scale=w.scale, tau=args.tau)
+        elif args.fp8_blocks:
+            if do_bwd:
+                sys.exit("--fp8-blocks profiles the forward only: add --fwd-only")
+            from workloads import quantise_e4m3_blocks
+            (qb8, qbf), (kb8, kbf), (vb8, vbf) = (quantise_e4m3_blocks(t.cpu()) for t in (q, k, v))
+            qb8, kb8, vb8, qbf, kbf, vbf = (t.to(dev) for t in (qb8, kb8, vb8, qbf, kbf, vbf))
+
+            def fwd():
+                fa.fa_fwd_fp8_blocks(qb8, kb8, vb8, qbf, kbf, vbf, o, lse, causal=w.causal, scale=w.scale,
+                                     tau=args.tau)
         elif args.mxfp4:
             if do_bwd:
                 sys.exit("--mxfp4 profiles the forward only: add --fwd-only")
@@ -239,6 +251,7 @@ def main():
         torch.cuda.synchronize()
         print(f"ran {args.reps} steps of {w.name}" + (" (e4m3 forward)" if args.fp8 else "") +
               (" (MXFP4 forward)" if args.mxfp4 else "") +
+              (" (e4m3 forward, block factors)" if args.fp8_blocks else "") +
               (f" after {args.reps} copies of {args.copy_mib} MiB" if args.copy_mib else ""), flush=True)
         return
 
