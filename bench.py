@@ -73,6 +73,52 @@ def parse():
     return p.parse_args()
 
 
+class ClockSampler:
+    """Samples the GPU's shader (GFX) clock every 20 ms from a side thread
+    through the amdsmi library while the step runs (the sustained warm-up and
+    the timed steps); mean / min / max in MHz, or None where the library or
+    the device does not report it."""
+
+    def __init__(self):
+        import threading
+        self.samples, self._stop = [], threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = amdsmi.amdsmi_get_processor_handles()[0]
+                while not self._stop.is_set():
+                    self.samples.append(float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]))
+                    time.sleep(0.02)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self):
+        s = self.samples
+        if not s:
+            return None
+        # the warm-up synchronises between batches, so some samples catch the
+        # clock dropping while the GPU waits: the median is taken over the
+        # samples at 1 GHz or more (the GPU at work)
+        busy = sorted(x for x in s if x >= 1000.0)
+        return {"busy_median_mhz": busy[len(busy) // 2] if busy else None, "max_mhz": max(s),
+                "busy_samples": len(busy), "samples": len(s),
+                "source": "amdsmi GFX clock, sampled every 20 ms during the warm-up and the timed steps"}
+
+
 def warm_gpu(fn, seconds):
     """Call fn() repeatedly for about `seconds` of wall time (untimed).  Under
     sustained load the MI355X shader clock settles within a fraction of a
@@ -272,6 +318,8 @@ def main():
         for _, fn in parts:
             fn()
 
+    sclk = ClockSampler()
+    sclk.__enter__()
     warm_gpu(step, args.warm_seconds)
     for _ in range(args.warmup):
         for _, fn in parts:
@@ -286,7 +334,9 @@ def main():
             e[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall0
-    part_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(len(parts))]
+    sclk.__exit__(None, None, None)
+    part_all = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(len(parts))]
+    part_ms = [sum(x) / args.steps for x in part_all]
     step_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
 
     # counted FLOPs (the configs' convention) and each kernel's own algorithmic
@@ -299,11 +349,13 @@ def main():
     work = {"fwd_kernel": ("mfma", 4 * d * pairs), "bwd_dq_kernel": ("mfma", 6 * d * pairs),
             "bwd_dkdv_kernel": ("mfma", 8 * d * pairs)}
     kernels = {}
-    for (name, _), ms in zip(parts, part_ms):
+    for i, ((name, _), ms) in enumerate(zip(parts, part_ms)):
         bound, amount = work[name]
         rate = amount / (ms * 1e-3) / (1e12 if bound == "mfma" else 1e9)
         peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
-        kernels[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(rate, 2),
+        xs = sorted(part_all[i])
+        kernels[name] = {"ms": round(ms, 5), "ms_median": round(xs[len(xs) // 2], 5), "ms_min": round(xs[0], 5),
+                         "ms_max": round(xs[-1], 5), "bound": bound, "achieved": round(rate, 2),
                          "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(rate / peak, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     kd = kernels[dom]
@@ -500,6 +552,8 @@ def main():
         "peak_tflops": PEAK_BF16_TFLOPS,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "gpu_over_cpu_oracle": round(value / cpu["value"], 1) if cpu and cpu.get("value") else None,
+        "sclk_observed": sclk.summary(),
         "kernels": kernels,
         "workloads_fwd": extra,
         "wall_s_timed": round(wall_s, 4),
