@@ -447,13 +447,16 @@ def main():
                 # the conditional rescale observed: wavefront-level corrections
                 # after each wavefront's first tile (instrumented forward), at
                 # tau = 8 and at tau = 0 (every rise of a wavefront's max)
-                ev = torch.zeros((ww.B, ww.H), dtype=torch.int32, device=dev)
+                ev = torch.zeros((ww.B, ww.H, -(-ww.Sq // 32)), dtype=torch.int32, device=dev)
                 counts = {}
                 for tau_c in (8.0, 0.0):
                     ev.zero_()
                     fa.fa_fwd_rescale_count(qq, kk, vv, oo, ll, ev, causal=ww.causal, scale=ww.scale, tau=tau_c)
                     torch.cuda.synchronize()
                     counts[f"tau{tau_c:g}"] = int(ev.sum().item())
+                    # wavefronts by their number of corrections: 0, 1, 2, ... (last bin: 7 or more)
+                    hist = torch.bincount(ev.flatten().clamp(max=7).long(), minlength=8)
+                    counts[f"tau{tau_c:g}_wavefront_histogram"] = hist.cpu().tolist()
                 # (wavefront, tile) steps after the first: each 32-row wavefront
                 # visits ceil(visible keys / 128) tiles of 128 keys
                 import math as _m

@@ -130,12 +130,17 @@ def fa_fwd(q, k, v, o, lse, causal=False, scale=None, tau=8.0, emu_frac=0.0):
         raise FAError(st, "fa_fwd")
 
 
+FA_RESCALE_SLOT_ROWS = 32
+
+
 def fa_fwd_rescale_count(q, k, v, o, lse, events, causal=False, scale=None, tau=8.0):
     """The instrumented forward (hardware exponentials): fills o and lse as
-    fa_fwd does and adds, per (b, h), the wavefront-level corrections taken
-    after each wavefront's first key tile to events (int32 CUDA [B, H])."""
+    fa_fwd does and adds, per (b, h) and 32-row wavefront slot, the
+    wavefront-level corrections taken after each wavefront's first key tile
+    to events (int32 CUDA [B, H, ceil(Sq / 32)])."""
     import torch
     B, H, Sq, d = q.shape
+    slots = -(-Sq // FA_RESCALE_SLOT_ROWS)
     Sk = k.shape[2]
     _check_bf16("q", q, (B, H, Sq, d))
     _check_bf16("k", k, (B, H, Sk, d))
@@ -143,8 +148,8 @@ def fa_fwd_rescale_count(q, k, v, o, lse, events, causal=False, scale=None, tau=
     _check_bf16("o", o, (B, H, Sq, d))
     _check_f32("lse", lse, (B, H, Sq))
     if events.dtype != torch.int32 or not events.is_cuda or not events.is_contiguous() or \
-            tuple(events.shape) != (B, H):
-        raise ValueError(f"events: expected a contiguous int32 CUDA tensor of shape {(B, H)}")
+            tuple(events.shape) != (B, H, slots):
+        raise ValueError(f"events: expected a contiguous int32 CUDA tensor of shape {(B, H, slots)}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_rescale_count(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,

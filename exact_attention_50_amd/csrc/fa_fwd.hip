@@ -72,7 +72,7 @@ struct FwdParams {
   int n_qblocks;
   float scale_log2;  // scale * log2(e)
   float tau;
-  unsigned* events;  // counting instantiation: corrections per (b, h), added to
+  unsigned* events;  // counting instantiation: corrections per (b, h, 32-row slot), added to
 };
 
 // LDS of the 256-row form: K ring of 2 stages, then V ring of 2 stages, each
@@ -100,9 +100,11 @@ constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
 // end.  Twice as many workgroups of half the size let the scheduler pair
 // heavy causal blocks with light ones when one 256-row block per CU would
 // leave the chip waiting on the heaviest.
-// COUNT: the instrumented instantiation adds, per (b, h), the number of
+// COUNT: the instrumented instantiation adds, per (b, h) and 32-row
+// wavefront slot (rows 32 i .. 32 i + 31 of the head), the number of
 // (wavefront, tile) steps after the wavefront's first tile in which the
-// correction branch was taken to p.events.
+// correction branch was taken to p.events[(b H + h) n_slots + i] (in the
+// split form both wave groups of those rows add to the slot).
 template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT = false>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   using L = FwdLayout<D, SPLIT>;
@@ -464,7 +466,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   }
   if constexpr (COUNT) {
     // one vector atomic per wavefront (lane 0 holds the address)
-    if (lane == 0 && n_events > 0) atomicAdd(p.events + bh, (unsigned)n_events);
+    if (lane == 0 && n_events > 0 && q_wave_lo < p.Sq)
+      atomicAdd(p.events + (size_t)bh * ((p.Sq + kQW - 1) / kQW) + q_wave_lo / kQW, (unsigned)n_events);
   }
   float l_lane = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   // this lane's query r32 from lane r32 % 16 (row 0: queries 0-15, row 1: 16-31)

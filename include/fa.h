@@ -80,16 +80,19 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  * the conditional rescale observable (the FlashAttention-4 summary, Key
  * claims §3.1.4, Eq. 6: the correction is gated per warp; here per
  * wavefront of 32 query rows).  Writes O and LSE exactly as fa_fwd with
- * emu_frac = 0 does, and adds to events[b * H + h], for each wavefront of
- * head (b, h), the number of its key tiles after its first one in which the
- * correction branch ran (some row of the wavefront saw its max rise by more
- * than tau over the reference max).  Tiles are those of the launch form
+ * emu_frac = 0 does, and adds to events[(b * H + h) * ceil(Sq / 32) + i],
+ * for the wavefront of rows 32 i .. 32 i + 31 of head (b, h), the number of
+ * its key tiles after its first one in which the correction branch ran (some
+ * row of the wavefront saw its max rise by more than tau over the reference
+ * max); in the few-blocks causal form two wavefronts share those rows and
+ * both add to the slot.  Tiles are those of the launch form
  * fa_fwd picks for the same shape: 128 keys per tile visited in order when
  * ceil(Sq / 256) * B * H >= 512 or non-causal; otherwise (few causal
  * blocks) each wavefront visits every other 64-key tile and its first tile
  * is the first it visits.
- *   events   device uint32 [B, H], 4-byte aligned, caller-owned; the call
- *            adds to it (zero it first), with atomics, so counts are exact.
+ *   events   device uint32 [B, H, ceil(Sq / 32)], 4-byte aligned,
+ *            caller-owned; the call adds to it (zero it first), with atomics,
+ *            so counts are exact.
  *   Other arguments and errors as for fa_fwd.
  * Returns FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED or FA_ERR_HIP. */
 fa_status fa_fwd_rescale_count(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,

@@ -45,6 +45,7 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
       row_rescales   int array [B,H,Sq]: corrections applied to a row (its max
                      rose by more than tau), after its first block
       group_events   number of (group, block) corrections after the first block
+      group_counts   int array [B,H,ceil(Sq/group_rows)]: the same per group
       rising_steps   number of (row, block) steps where the row max rose,
                      after the first block
       max_p          largest unnormalised probability seen (<= 2^tau)
@@ -57,6 +58,7 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
     O = np.empty((B, H, Sq, v.shape[3]))
     LSE = np.empty((B, H, Sq))
     row_rescales = np.zeros((B, H, Sq), dtype=np.int64)
+    group_counts = np.zeros((B, H, (Sq + group_rows - 1) // group_rows), dtype=np.int64)
     group_events = 0
     rising_steps = 0
     max_p = 0.0
@@ -85,6 +87,7 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
                     ng = need[g]
                     if blk > 0:
                         group_events += 1
+                        group_counts[b, h, g0 // group_rows] += 1
                         row_rescales[b, h, g] += ng
                     with np.errstate(invalid="ignore"):
                         alpha = np.where(np.isfinite(m_ref[g]),
@@ -102,6 +105,6 @@ def conditional_rescale_forward(q, k, v, scale, causal=False, tau=8.0,
             O[b, h] = acc / l[:, None]
             LSE[b, h] = (m_ref + np.log2(l)) * LN2
             min_l = min(min_l, float(l.min()))
-    stats = dict(row_rescales=row_rescales, group_events=group_events,
+    stats = dict(row_rescales=row_rescales, group_events=group_events, group_counts=group_counts,
                  rising_steps=rising_steps, max_p=max_p, min_l=min_l)
     return O, LSE, stats

@@ -93,3 +93,11 @@ def test_group_size_changes_event_count_only():
     assert np.array_equal(s1["row_rescales"], s32["row_rescales"])
     assert np.array_equal(O1, O32) and np.array_equal(L1, L32)
     assert s32["group_events"] <= s1["group_events"] == s1["row_rescales"].sum()
+    # per-group counts: with one row per group they are the row counts; a
+    # group corrects in a block iff one of its rows does, so its count lies
+    # between its rows' largest count and their sum
+    assert np.array_equal(s1["group_counts"], s1["row_rescales"])
+    assert s32["group_counts"].sum() == s32["group_events"]
+    rows = s1["row_rescales"].reshape(s1["row_rescales"].shape[:2] + (-1, 32))
+    assert np.all(rows.max(-1) <= s32["group_counts"]) and np.all(s32["group_counts"] <= rows.sum(-1))
+    assert s32["group_counts"].max() > 0
