@@ -4,11 +4,13 @@
 One step = fa_fwd followed by the backward (every step of the forward and
 the backward path) on the bwd workload: B=1, H=16, Sq=Sk=4096, d=128,
 causal, bf16 inputs drawn by workloads.py (seed 5), O and LSE taken from
-fa_fwd.  The backward is enqueued as its two launches (fa_bwd_phase with
-PREPARE | DQ, whose dQ kernel also forms the row terms, then DKDV: the same
-launches fa_bwd makes) with HIP events between them, on the stream the
-kernels run on, so each kernel's average duration is measured inside the
-timed region.  Inputs and outputs are resident in device
+fa_fwd.  The backward is the five-product form (--bwd ds, the default:
+fa_bwd_ds, enqueued as its three launches PREPARE, DKDV, DQ through
+fa_bwd_ds_phase) or the split form (--bwd split: fa_bwd's two launches,
+PREPARE | DQ, whose dQ kernel also forms the row terms, then DKDV), with HIP
+events between the launches, on the stream the kernels run on, so each
+kernel's average duration is measured inside the timed region; the form not
+in the step is timed beside it.  Inputs and outputs are resident in device
 memory before timing starts.
 
 Printed: ONE JSON line with the throughput in TFLOP/s (counted FLOPs:
@@ -56,6 +58,8 @@ def parse():
     p.add_argument("--tau", type=float, default=8.0)
     p.add_argument("--emu", type=float, default=0.0)
     p.add_argument("--deterministic", type=int, default=0)
+    p.add_argument("--bwd", choices=("ds", "split"), default="ds",
+                   help="backward of the step: five-product (fa_bwd_ds) or split by output (fa_bwd)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the per-workload forward sweep")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle sample")
@@ -150,7 +154,8 @@ def time_calls(fn, n, warmup, warm_s=0.0):
 
 # the source file of each kernel; every kernel also depends on the shared headers
 KERNEL_SOURCE = {"fwd_kernel": "fa_fwd.hip", "bwd_prep_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip",
-                 "bwd_dkdv_kernel": "fa_bwd.hip", "merge_kernel": "fa_merge.hip", "fwd8_kernel": "fa_fwd8.hip"}
+                 "bwd_dkdv_kernel": "fa_bwd.hip", "bwd_dkdv_kernel_ds": "fa_bwd.hip",
+                 "bwd_dq_ds_kernel": "fa_bwd.hip", "merge_kernel": "fa_merge.hip", "fwd8_kernel": "fa_fwd8.hip"}
 
 
 def kernel_sources_sha256(kernel):
@@ -242,13 +247,22 @@ def main():
     ws = torch.empty(max(16, fa.fa_bwd_workspace_bytes(B, H, Sq, Sk, d, w.causal, args.deterministic)),
                      dtype=torch.uint8, device=dev)
     do_bwd = not args.fwd_only
+    ws_ds = None
+    if do_bwd:
+        ws_ds = torch.empty(fa.fa_bwd_ds_workspace_bytes(B, H, Sq, Sk, d, w.causal, args.deterministic),
+                            dtype=torch.uint8, device=dev)
 
     def fwd():
         fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, tau=args.tau, emu_frac=args.emu)
 
-    def bwd():
-        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
-                  deterministic=bool(args.deterministic))
+    def bwd_split(det=args.deterministic):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale, deterministic=bool(det))
+
+    def bwd_ds(det=args.deterministic):
+        fa.fa_bwd_ds(q, k, v, o, lse, do, dq, dk, dv, ws_ds, causal=w.causal, scale=w.scale,
+                     deterministic=bool(det))
+
+    bwd = bwd_ds if args.bwd == "ds" else bwd_split
 
     if args.reps:
         # profiler mode: optional plain copies of known size (to scale HBM
@@ -305,10 +319,20 @@ def main():
         fa.fa_bwd_phase(ph, q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
                         deterministic=bool(args.deterministic))
 
-    # the step, kernel by kernel, as fa_bwd launches it: PREPARE and DQ in one
-    # call (the dQ kernel forms the row terms D_i, LSE_i log2(e) itself), then DKDV
+    def bwd_ds_phase(ph):
+        fa.fa_bwd_ds_phase(ph, q, k, v, o, lse, do, dq, dk, dv, ws_ds, causal=w.causal, scale=w.scale,
+                           deterministic=bool(args.deterministic))
+
+    # the step, kernel by kernel, as the backward call launches it.  Five
+    # products: PREPARE (row terms), DKDV (dK, dV and dS), DQ (dQ from dS).
+    # Split: PREPARE and DQ in one call (the dQ kernel forms the row terms
+    # D_i, LSE_i log2(e) itself), then DKDV
     parts = [("fwd_kernel", fwd)]
-    if do_bwd:
+    if do_bwd and args.bwd == "ds":
+        parts += [("bwd_prep_kernel", lambda: bwd_ds_phase(fa.FA_BWD_PREPARE)),
+                  ("bwd_dkdv_kernel_ds", lambda: bwd_ds_phase(fa.FA_BWD_DKDV)),
+                  ("bwd_dq_ds_kernel", lambda: bwd_ds_phase(fa.FA_BWD_DQ))]
+    elif do_bwd:
         parts += [("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_PREPARE | fa.FA_BWD_DQ)),
                   ("bwd_dkdv_kernel", lambda: bwd_phase(fa.FA_BWD_DKDV))]
 
@@ -341,13 +365,23 @@ def main():
 
     # counted FLOPs (the configs' convention) and each kernel's own algorithmic
     # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ; its row
-    # terms are O(rows d) beside them); dK/dV kernel 8d (S, dP, dV, dK)
+    # terms are O(rows d) beside them); dK/dV kernel 8d (S, dP, dV, dK), with
+    # or without the dS stores.  HBM-bound kernels: algorithmic bytes, each
+    # input read once and each output written once -- the prep kernel reads O
+    # and dO (bf16) and LSE, writes D and LSE log2(e); the dQ-from-dS kernel
+    # reads the dS tiles of its blocks (2 bytes per (query, key) pair of the
+    # 128 x 64 tiles it visits) and K, writes dQ
     pairs = w.flops("fwd") / (4 * d)
     f_fwd = w.flops("fwd")
     f_bwd = w.flops("bwd") if do_bwd else 0.0
     value = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    rows = B * H * Sq
+    n_kt = -(-Sk // 64)
+    ds_tiles = sum(min(n_kt, 2 * (qb + 1)) if w.causal else n_kt for qb in range(-(-Sq // 128)))
     work = {"fwd_kernel": ("mfma", 4 * d * pairs), "bwd_dq_kernel": ("mfma", 6 * d * pairs),
-            "bwd_dkdv_kernel": ("mfma", 8 * d * pairs)}
+            "bwd_dkdv_kernel": ("mfma", 8 * d * pairs), "bwd_dkdv_kernel_ds": ("mfma", 8 * d * pairs),
+            "bwd_prep_kernel": ("hbm", rows * (2 * d * 2 + 4 + 8)),
+            "bwd_dq_ds_kernel": ("hbm", B * H * ds_tiles * 128 * 64 * 2 + B * H * Sk * d * 2 + rows * d * 2)}
     kernels = {}
     for i, ((name, _), ms) in enumerate(zip(parts, part_ms)):
         bound, amount = work[name]
@@ -520,14 +554,15 @@ def main():
         del qq, kk, vv, op, lp, om, lm
 
     if do_bwd and not args.no_extra:
-        # the deterministic flag selects the same kernels (every output element
-        # is written once by one workgroup in a fixed order): both timed
+        # both backward forms as whole calls, each in both modes: the
+        # deterministic flag selects the same kernels (every output element is
+        # written once by one workgroup in a fixed order)
         det_ab = {}
-        for det in (0, 1):
-            det_ab[f"deterministic{det}_bwd_ms"] = round(time_calls(
-                lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=w.causal, scale=w.scale,
-                                  deterministic=bool(det)), max(10, args.steps), 3, args.warm_seconds / 3), 5)
-        extra["bwd_deterministic_ab"] = det_ab
+        for form, fn in (("ds", bwd_ds), ("split", bwd_split)):
+            for det in (0, 1):
+                det_ab[f"{form}_deterministic{det}_bwd_ms"] = round(time_calls(
+                    lambda: fn(det), max(10, args.steps), 3, args.warm_seconds / 3), 5)
+        extra["bwd_forms_and_deterministic_ab"] = det_ab
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -550,7 +585,8 @@ def main():
         "config": {"workload": w.name + ("" if do_bwd else " (forward only)"), "B": B, "H": H, "Sq": Sq,
                    "Sk": Sk, "d": d, "causal": w.causal, "tau": args.tau, "emu_frac": args.emu,
                    "deterministic_bwd": bool(args.deterministic),
-                   "step": "fa_fwd + fa_bwd" if do_bwd else "fa_fwd"},
+                   "step": ("fa_fwd + " + ("fa_bwd_ds" if args.bwd == "ds" else "fa_bwd")) if do_bwd
+                   else "fa_fwd"},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "peak_tflops": PEAK_BF16_TFLOPS,
         "roofline": roof,

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
     "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
-    "backward", "fa_bwd_noalloc", "fa_fwd_mxfp4", "forward_mxfp4", "fa_fwd_fp8_blocks", "forward_fp8_blocks",
+    "backward", "fa_bwd_noalloc", "fa_bwd_ds", "fa_bwd_ds_phase", "fa_bwd_ds_workspace_bytes", "backward_ds", "fa_fwd_mxfp4", "forward_mxfp4", "fa_fwd_fp8_blocks", "forward_fp8_blocks",
     "LIB_PATH",
 ]
 
@@ -69,6 +69,12 @@ def lib():
     L.fa_bwd_noalloc.restype = i
     L.fa_bwd_phase.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_bwd_phase.restype = i
+    L.fa_bwd_ds_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.fa_bwd_ds_workspace_bytes.restype = sz
+    L.fa_bwd_ds.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_bwd_ds.restype = i
+    L.fa_bwd_ds_phase.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_bwd_ds_phase.restype = i
     L.fa_exp2_probe.argtypes = [vp, vp, vp, ctypes.c_longlong, vp]
     L.fa_exp2_probe.restype = i
     L.fa_status_str.argtypes = [i]
@@ -313,6 +319,60 @@ def fa_bwd_phase(phases, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=Fa
                             int(bool(deterministic)), _ptr(workspace), ws_bytes, _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_bwd_phase")
+
+
+def fa_bwd_ds_workspace_bytes(B, H, Sq, Sk, d, causal, deterministic):
+    return int(lib().fa_bwd_ds_workspace_bytes(B, H, Sq, Sk, d, int(bool(causal)), int(bool(deterministic))))
+
+
+def _bwd_call(name, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, deterministic, phases=None):
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    for n, t, s in (("q", q, (B, H, Sq, d)), ("k", k, (B, H, Sk, d)), ("v", v, (B, H, Sk, d)),
+                    ("o", o, (B, H, Sq, d)), ("dout", dout, (B, H, Sq, d)), ("dq", dq, (B, H, Sq, d)),
+                    ("dk", dk, (B, H, Sk, d)), ("dv", dv, (B, H, Sk, d))):
+        _check_bf16(n, t, s)
+    _check_f32("lse", lse, (B, H, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    head = () if phases is None else (int(phases),)
+    st = getattr(lib(), name)(*head, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, Sq, Sk, d, int(bool(causal)), float(scale), int(bool(deterministic)),
+                              _ptr(workspace), ws_bytes, _stream(q))
+    if st != FA_OK:
+        raise FAError(st, name)
+
+
+def fa_bwd_ds(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, deterministic=False):
+    """Enqueue the five-product backward (dS through the workspace) on the
+    current stream; fills dq, dk, dv in place."""
+    _bwd_call("fa_bwd_ds", q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, deterministic)
+
+
+def fa_bwd_ds_phase(phases, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None,
+                    deterministic=False):
+    """Enqueue some of fa_bwd_ds's launches (FA_BWD_PREPARE, then FA_BWD_DKDV,
+    then FA_BWD_DQ) on the current stream."""
+    _bwd_call("fa_bwd_ds_phase", q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, deterministic,
+              phases=phases)
+
+
+def backward_ds(q, k, v, o, lse, dout, causal=False, scale=None, deterministic=False, workspace=None):
+    """Five-product backward; returns (dQ, dK, dV) bf16."""
+    import torch
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if workspace is None:
+        nbytes = fa_bwd_ds_workspace_bytes(B, H, Sq, Sk, d, causal, deterministic)
+        if nbytes == 0:
+            raise FAError(FA_ERR_UNSUPPORTED, "fa_bwd_ds_workspace_bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    fa_bwd_ds(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=causal, scale=scale, deterministic=deterministic)
+    return dq, dk, dv
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, deterministic=False):

@@ -276,6 +276,58 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                       workspace, workspace_bytes, stream);
 }
 
+namespace {
+// dS^T of one (b, h) slice within a 2^31-byte buffer range (32-bit offsets)
+bool ds_addressable(int Sq, int Sk) {
+  const long long nqb = (Sq + 127) / 128, rows = (Sk + 127) / 128 * 128LL;
+  return nqb * rows * 128 * 2 < (1LL << 31);
+}
+}  // namespace
+
+size_t fa_bwd_ds_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic) {
+  (void)causal;
+  (void)deterministic;
+  if (!sizes_ok(B, H, Sq, Sk) || !d_supported(d) || !ds_addressable(Sq, Sk)) return 0;
+  return fa::bwd_ds_workspace_bytes(B, H, Sq, Sk);
+}
+
+fa_status fa_bwd_ds_phase(int phases, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                          const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d,
+                          int causal, float scale, int deterministic, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (phases < 1 || phases > FA_BWD_ALL) return FA_ERR_INVALID;
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_INVALID;
+  const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID;
+  if (!sizes_ok(B, H, Sq, Sk)) return FA_ERR_INVALID;
+  if (!(isfinite(scale) && scale > 0.0f)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (deterministic != 0 && deterministic != 1) return FA_ERR_INVALID;
+  if (!d_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return FA_ERR_UNSUPPORTED;
+  if (!head_addressable(Sq, Sk, d) || !ds_addressable(Sq, Sk)) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::bwd_ds_workspace_bytes(B, H, Sq, Sk)) return FA_ERR_INVALID;
+
+  fa::BwdArgs a;
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE; a.dout = dO;
+  a.dq = dQ; a.dk = dK; a.dv = dV;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.deterministic = deterministic != 0;
+  a.workspace = workspace;
+  const hipError_t e = fa::launch_bwd_ds(a, phases, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd_ds(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                    void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d, int causal, float scale,
+                    int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ds_phase(FA_BWD_ALL, Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, Sq, Sk, d, causal, scale,
+                         deterministic, workspace, workspace_bytes, stream);
+}
+
 fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                          const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Sq, int Sk, int d,
                          int causal, float scale, int deterministic, void* stream) {

@@ -24,6 +24,14 @@
 // modes (the deterministic flag costs nothing).  Tiles use the layout of
 // fa_tiles.hpp, so Q, dO, K and V are each read both row-wise and transposed
 // from one LDS copy.
+//
+// Five-product form (fa_bwd_ds): the paper's five products per tile pair
+// without its dQ atomics.  bwd_dkdv_kernel, which rounds dS to bf16 for its
+// dK product anyway, also stores it to a dS^T buffer in the workspace, and
+// bwd_dq_ds_kernel forms dQ = scale dS K from that buffer and K: S and dP
+// are formed once, at the price of writing and reading dS (2 bytes per
+// visited pair) through HBM.  Also free of atomics and bit-identical run to
+// run.
 
 #include <mutex>
 #include <type_traits>
@@ -47,11 +55,26 @@ struct BwdParams {
   bf16* dv;
   float* dvec;   // D_i, [B, H, Sq]
   float* lse2;   // LSE_i * log2(e), [B, H, Sq]
+  bf16* ds;      // five-product form: dS^T slabs, [B H, ds_nqb, ds_rows, 128]
+  int ds_nqb;    // blocks of 128 query rows, ceil(Sq / 128)
+  int ds_rows;   // key rows per slab, Sk rounded up to 128
   int BH, Sq, Sk;
   int fuse_prep; // the dQ kernel forms D_i and LSE_i log2(e) itself and stores them
   float scale;
   float scale_log2;
 };
+
+// dS^T buffer of the five-product form.  Per (b, h) and block of 128 query
+// rows ("positions", one dQ workgroup each) a slab of 8 groups of 16
+// positions; in group pg, key row k holds positions 16 pg .. +16 as one
+// 32-byte record at byte (pg * ds_rows + k) * 32.  Position 16 x + 8 g + j
+// of a block holds query row 16 x + 8 (j / 4) + 4 g + j % 4 (bits 2 and 3 of
+// the row index exchanged): the order in which a lane of the dK/dV kernel
+// holds dS, so one of its 16-byte stores of a 16-row step covers half a
+// record and a wave's store (32 keys) 1 KB of consecutive records.
+constexpr int kDsPositions = 128;
+constexpr int kDsGroup = 16;                                // positions per record
+constexpr int kDsRecord = kDsGroup * 2;                     // bytes per record
 
 // ------------------------------------------------------------------- prep
 // D_i and LSE_i log2(e) of every query row into the workspace.
@@ -408,7 +431,8 @@ struct Layout {
 };
 }  // namespace kvk
 
-template <int D, bool CAUSAL>
+// DS: also store the tile's bf16 dS (the five-product form).
+template <int D, bool CAUSAL, bool DS = false>
 __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   using namespace kvk;
   using L = Layout<D>;
@@ -455,6 +479,15 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 
   const int row_lane = row_lane_offset<D>(lane);
   const int tr_lane = tr_lane_offset<D>(lane);
+
+  // DS: the lane's dS values of a 16-row step (rows 8 (j / 4) + 4 g + j % 4,
+  // j < 8) are half g of its key's record in the step's position group of
+  // the tile's 128-row query block: one 16-byte buffer store whose per-tile
+  // part is a scalar offset
+  const size_t ds_slab = (size_t)p.ds_rows * kDsPositions;
+  const __amdgpu_buffer_rsrc_t rds =
+      make_rsrc(DS ? p.ds + (size_t)bh * p.ds_nqb * ds_slab : nullptr, DS ? (unsigned)(p.ds_nqb * ds_slab * 2) : 0u);
+  const int ds_lane = key * kDsRecord + 16 * g;
 
   // B operands: the lane's K and V rows, dims 16 kc + 8 g .. +8
   bf16x8 kf[kKC], vf[kKC];
@@ -584,6 +617,19 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
           issue_one(t + 2, std::integral_constant<int, (decltype(stage_tag)::value + 2) % kStages>{},
                     std::integral_constant<int, kEarly + j>{});
       }
+      // DS: the four bf16 dS steps of this tile, after the barrier (so a
+      // whole tile passes before the next vmcnt wait, which counts them too)
+      // and before the next tile repacks them.  Non-temporal stores: dS is
+      // read once, by the other kernel, and left in the L2 it would evict
+      // the Q / dO tiles every key block of the head re-reads (measured:
+      // +35 MiB of refetches per launch with ordinary stores)
+      if constexpr (DS && j >= kSteps - 4) {
+        constexpr int x = j - (kSteps - 4);
+        constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
+        const int pg = (q0 % kDsPositions) / kDsGroup + x;
+        const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) + pg * p.ds_rows * kDsRecord;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
+      }
       const bf16x8 a = ring[j % kRing];
       if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, j + kRing);
       else ring[j % kRing] = op(nxt, j + kRing - kSteps);
@@ -676,6 +722,144 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
             lane);
 }
 
+// ============================================================ dQ from dS
+// Five-product form: dQ = scale dS K from the dS^T buffer (layout above) and
+// K.  A workgroup owns one slab (128 query rows) and streams 64-key tiles of
+// K and of the slab, memory-to-LDS, through a ring of kStages stages issued
+// kStages - 1 tiles ahead; per tile and wave (positions 32 w .. +32):
+//   dQ^T (D x 32) += K^T (D x 64 keys) . dS^T (64 keys x 32),
+// both operands read transposed, so their k slots (keys) follow one order.
+// The K tile has the layout of fa_tiles.hpp.  The dS tile is the slab's 8
+// groups x 64 records (2 KB per group); in odd groups record r holds key
+// r ^ 4, so the two 16-lane halves of a transposed read pass (groups 2 w and
+// 2 w + 1, same keys) meet opposite halves of the 64 banks.  A tile's loads
+// are spread over its products (a memory-to-LDS load stalls the issuing
+// wave for a while), and each product's operands are read a step ahead.
+// The dS loads carry the non-temporal hint (dS is read once; K stays).
+// Causal: the slab of block qb needs keys 0 .. 128 qb + 127 only (dS is zero
+// past the diagonal, and those are exactly the tiles the dK/dV kernel
+// wrote).  HBM-bound: dS is read once.
+namespace dsk {
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;
+constexpr int kStages = 4;
+constexpr int kSBytes = kBN * kDsRecord * (kDsPositions / kDsGroup);   // 16 KB
+constexpr int kSLoads = kSBytes / 1024 / kWaves;                        // per wave
+template <int D>
+struct Layout {
+  static constexpr int kKBytes = kBN * TileGeom<D>::kRowBytes;
+  static constexpr int kStageBytes = kKBytes + kSBytes;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kKLoads = TileDMA<D, kBN, kWaves>::kLoads;
+  static constexpr int kPer = kKLoads + kSLoads;
+};
+}  // namespace dsk
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p) {
+  using namespace dsk;
+  using L = Layout<D>;
+  constexpr int kDB = D / 32;
+  constexpr int kPer = L::kPer;
+  constexpr int kSteps = (kBN / 16) * kDB;   // products per tile and wave
+  static_assert(kWaves * 32 == kDsPositions, "one 32-position block per wave");
+  static_assert(kPer <= kSteps, "one load per product at most");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = p.ds_nqb - 1 - (int)blockIdx.x / p.BH;   // most key tiles first when causal
+  const int bh = (int)blockIdx.x % p.BH;
+  const int n_all = (p.Sk + kBN - 1) / kBN;
+  const int n = CAUSAL ? min(n_all, (qb + 1) * (kDsPositions / kBN)) : n_all;
+
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(p.k + (size_t)bh * p.Sk * D, (unsigned)p.Sk * TileGeom<D>::kRowBytes);
+  const size_t slab = (size_t)p.ds_rows * kDsPositions;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ds + ((size_t)bh * p.ds_nqb + qb) * slab, (unsigned)(slab * 2));
+  const int tr_k = tr_lane_offset<D>(lane);
+  // dS load i of this wave: 1 KB of LDS = records 32 (blk % 2) .. +32 of group
+  // blk / 2, blk = 4 i + w; lane l fetches half l % 2 of record 32 (blk % 2) + l / 2
+  auto s_src = [&](int t, int i) __attribute__((always_inline)) -> unsigned {
+    const int blk = i * kWaves + wave;
+    const int pg = blk >> 1;
+    const int rec = ((blk & 1) * 32 + (lane >> 1)) ^ (4 * (pg & 1));
+    return (unsigned)((pg * p.ds_rows + t * kBN + rec) * kDsRecord + 16 * (lane & 1));
+  };
+  // B operand (dS^T, k = keys of step ks in accumulator order, n = position
+  // 32 w + lane % 32): two ds_read_b64_tr_b16 over 4 records x 16 positions of
+  // group pg = 2 w + h, h = (lane / 16) % 2; rows 16 ks + 4 g + s / 4 (and + 8)
+  const int s16 = lane & 15, hh = (lane >> 4) & 1, gg = lane >> 5;
+  const int tr_s = ((2 * wave + hh) * kBN + 4 * (gg ^ hh) + (s16 >> 2)) * kDsRecord + 8 * (s16 & 3);
+  auto read_s = [&](const char* stile, int ks) __attribute__((always_inline)) -> bf16x8 {
+    const bf16x4_t lo = lds_read_tr16(stile + tr_s + 16 * ks * kDsRecord);
+    const bf16x4_t hi = lds_read_tr16(stile + tr_s + (16 * ks + 8) * kDsRecord);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto load_one = [&](int t, int i) __attribute__((always_inline)) {
+    char* st = smem + (t % kStages) * L::kStageBytes;
+    if (i < L::kKLoads) {
+      TileDMA<D, kBN, kWaves>::load_one(rk, t * kBN, st, wave, lane, i);
+    } else {
+      const int j = i - L::kKLoads;
+      lds_dma16_stream(rs, s_src(t, j), st + L::kKBytes + (j * kWaves + wave) * 1024);
+    }
+  };
+
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) acc[db] = f32x16{};
+
+  constexpr int kLead = kStages - 1;   // tiles in flight ahead of the one in use
+  static_for<kLead>([&](auto U) __attribute__((always_inline)) {
+    if (U < n) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) load_one(U, i);
+    }
+  });
+  for (int t = 0; t < n; ++t) {
+    // tile t is complete once at most the loads of the (up to kLead - 1)
+    // tiles issued after it are outstanding; the barrier also ends every
+    // wave's reads of tile t - 1, whose stage tile t + kLead takes
+    const int after = min(n - 1 - t, kLead - 1);
+    static_for<kLead>([&](auto U) __attribute__((always_inline)) {
+      if (after == U) wait_vmcnt<U * kPer>();
+    });
+    lds_barrier();
+    const char* kt = smem + (t % kStages) * L::kStageBytes;
+    const char* stile = kt + L::kKBytes;
+    const bool more = t + kLead < n;
+    bf16x8 a_cur = read_cols<D>(kt, tr_k, 0, 0);
+    bf16x8 b_cur = read_s(stile, 0);
+    static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = J;
+      constexpr int ks = j / kDB, db = j % kDB;
+      bf16x8 a_nxt = a_cur, b_nxt = b_cur;
+      if constexpr (j + 1 < kSteps) {
+        a_nxt = read_cols<D>(kt, tr_k, (j + 1) / kDB, (j + 1) % kDB);
+        if constexpr ((j + 1) % kDB == 0) b_nxt = read_s(stile, (j + 1) / kDB);
+      }
+      constexpr int every = kSteps / kPer;
+      if constexpr (j % every == 0 && j / every < kPer) {
+        if (more) load_one(t + kLead, j / every);
+      }
+      acc[db] = mfma32x32x16(a_cur, b_cur, acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      a_cur = a_nxt;
+      b_cur = b_nxt;
+      (void)ks;
+    });
+  }
+
+  // dQ = scale (dQ^T)^T -> bf16; lane r + 32 g holds position 32 w + r, i.e.
+  // query row 32 w + r with bits 2 and 3 exchanged
+  static_assert(kWaves * RowStore<D>::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+  dma_barrier();
+  RowStore<D>::store(smem + wave * RowStore<D>::kBytes, acc, p.scale, p.dq + (size_t)bh * p.Sq * D,
+                     qb * kDsPositions + 32 * wave, p.Sq, lane, /*swap23=*/true);
+}
+
 template <typename K>
 hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int lds, hipStream_t stream, const BwdParams& prm) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -718,6 +902,66 @@ hipError_t launch_all(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t 
   return e;
 }
 
+size_t ds_bytes(int B, int H, int Sq, int Sk) {
+  const size_t nqb = (size_t)((Sq + kDsPositions - 1) / kDsPositions);
+  const size_t rows = (size_t)((Sk + kvk::kBK - 1) / kvk::kBK) * kvk::kBK;
+  return (size_t)B * H * nqb * rows * kDsPositions * sizeof(bf16);
+}
+
+template <int D>
+hipError_t launch_ds(const BwdArgs& a, BwdParams& prm, int phases, hipStream_t stream) {
+  // workspace: the row terms as in launch_all, then the dS^T slabs
+  const size_t sec = ((size_t)a.B * a.H * a.Sq * sizeof(float) + 255) & ~size_t(255);
+  prm.dvec = static_cast<float*>(a.workspace);
+  prm.lse2 = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + sec);
+  prm.ds = reinterpret_cast<bf16*>(static_cast<char*>(a.workspace) + 2 * sec);
+  prm.ds_nqb = (a.Sq + kDsPositions - 1) / kDsPositions;
+  prm.ds_rows = (a.Sk + kvk::kBK - 1) / kvk::kBK * kvk::kBK;
+  prm.fuse_prep = 0;
+  hipError_t e = hipSuccess;
+  if (phases & kBwdPrepare) {
+    const long long rows = (long long)a.B * a.H * a.Sq;
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(1024), dim3(256), 0, stream, prm, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kBwdDkdv) {
+    const dim3 gk((unsigned)(((a.Sk + kvk::kBK - 1) / kvk::kBK) * prm.BH));
+    e = a.causal ? launch_dyn(bwd_dkdv_kernel<D, true, true>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes,
+                              stream, prm)
+                 : launch_dyn(bwd_dkdv_kernel<D, false, true>, gk, dim3(kvk::kThreads), kvk::Layout<D>::kLdsBytes,
+                              stream, prm);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kBwdDq) {
+    const dim3 gq((unsigned)(prm.ds_nqb * prm.BH));
+    e = a.causal ? launch_dyn(bwd_dq_ds_kernel<D, true>, gq, dim3(dsk::kThreads), dsk::Layout<D>::kLdsBytes,
+                              stream, prm)
+                 : launch_dyn(bwd_dq_ds_kernel<D, false>, gq, dim3(dsk::kThreads), dsk::Layout<D>::kLdsBytes,
+                              stream, prm);
+  }
+  return e;
+}
+
+BwdParams make_params(const BwdArgs& a) {
+  BwdParams prm{};
+  prm.q = static_cast<const bf16*>(a.q);
+  prm.k = static_cast<const bf16*>(a.k);
+  prm.v = static_cast<const bf16*>(a.v);
+  prm.o = static_cast<const bf16*>(a.o);
+  prm.lse = a.lse;
+  prm.dout = static_cast<const bf16*>(a.dout);
+  prm.dq = static_cast<bf16*>(a.dq);
+  prm.dk = static_cast<bf16*>(a.dk);
+  prm.dv = static_cast<bf16*>(a.dv);
+  prm.BH = a.B * a.H;
+  prm.Sq = a.Sq;
+  prm.Sk = a.Sk;
+  prm.scale = a.scale;
+  prm.scale_log2 = a.scale * kLog2e;
+  return prm;
+}
+
 }  // namespace
 
 // ------------------------------------------------- fixed scratch
@@ -755,22 +999,17 @@ size_t bwd_workspace_bytes(int B, int H, int Sq, int /*Sk*/, int /*d*/, bool /*d
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream) {
-  BwdParams prm;
-  prm.q = static_cast<const bf16*>(a.q);
-  prm.k = static_cast<const bf16*>(a.k);
-  prm.v = static_cast<const bf16*>(a.v);
-  prm.o = static_cast<const bf16*>(a.o);
-  prm.lse = a.lse;
-  prm.dout = static_cast<const bf16*>(a.dout);
-  prm.dq = static_cast<bf16*>(a.dq);
-  prm.dk = static_cast<bf16*>(a.dk);
-  prm.dv = static_cast<bf16*>(a.dv);
-  prm.BH = a.B * a.H;
-  prm.Sq = a.Sq;
-  prm.Sk = a.Sk;
-  prm.scale = a.scale;
-  prm.scale_log2 = a.scale * kLog2e;
+  BwdParams prm = make_params(a);
   return a.d == 64 ? launch_all<64>(a, prm, phases, stream) : launch_all<128>(a, prm, phases, stream);
+}
+
+size_t bwd_ds_workspace_bytes(int B, int H, int Sq, int Sk) {
+  return bwd_workspace_bytes(B, H, Sq, Sk, 128, false) + ds_bytes(B, H, Sq, Sk);
+}
+
+hipError_t launch_bwd_ds(const BwdArgs& a, int phases, hipStream_t stream) {
+  BwdParams prm = make_params(a);
+  return a.d == 64 ? launch_ds<64>(a, prm, phases, stream) : launch_ds<128>(a, prm, phases, stream);
 }
 
 }  // namespace fa

@@ -233,6 +233,12 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned vof
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voffset), "s"(r), "{m0}"(lds_addr(lds_dst)) : "memory");
 }
+// The same with the non-temporal hint: data read once, so its lines are the
+// first the L2 gives up (other data stays resident).
+__device__ __forceinline__ void lds_dma16_stream(__amdgpu_buffer_rsrc_t r, unsigned voffset, const void* lds_dst) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :: "v"(voffset), "s"(r), "{m0}"(lds_addr(lds_dst)) : "memory");
+}
 __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, unsigned voffset, const void* lds_dst) {
   asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :: "v"(voffset), "s"(r), "{m0}"(lds_addr(lds_dst)) : "memory");

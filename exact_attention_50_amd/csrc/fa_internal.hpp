@@ -91,6 +91,11 @@ hipError_t bwd_scratch(void** out);
 // phases: bit mask of the kernels to enqueue, in this order
 constexpr int kBwdPrepare = 1, kBwdDq = 2, kBwdDkdv = 4;
 hipError_t launch_bwd(const BwdArgs& a, int phases, hipStream_t stream);
+// Five-product backward: prep, dK/dV (also writing dS^T), dQ from dS, in
+// that order (phases: the kBwd* bits).  Its workspace: the row terms, then
+// ceil(Sq/128) slabs of [Sk rounded up to 128, 128] bf16 per (b, h).
+size_t bwd_ds_workspace_bytes(int B, int H, int Sq, int Sk);
+hipError_t launch_bwd_ds(const BwdArgs& a, int phases, hipStream_t stream);
 
 hipError_t launch_exp2_probe(const float* x, float* y_hw, float* y_emu, long long n, hipStream_t stream);
 

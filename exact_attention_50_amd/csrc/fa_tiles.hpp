@@ -137,22 +137,26 @@ struct TileDMA {
 // i.e. per row), is staged in `stage` (kBytes of LDS private to the wave, rows
 // padded by 16 bytes so the 8-byte writes meet every bank once per 16 rows)
 // and stored 16 bytes per lane over consecutive rows: rows row0 .. row0 + 31
-// of out (row pitch D elements), skipping rows >= n_rows.
+// of out (row pitch D elements), skipping rows >= n_rows.  With swap23 the
+// lane's row is r with bits 2 and 3 exchanged (lane r + 32 g holds row
+// (r & 19) | (r & 4) << 1 | (r & 8) >> 1): the row order of an accumulator
+// whose columns came from a transposed read of rows stored in that order.
 template <int D>
 struct RowStore {
   static constexpr int kPitch = D * 2 + 16;
   static constexpr int kBytes = 32 * kPitch;
 
   __device__ __forceinline__ static void store(char* stage, const f32x16* acc, float mul, bf16* out, int row0,
-                                               int n_rows, int lane) {
+                                               int n_rows, int lane, bool swap23 = false) {
     const int r = lane & 31, g = lane >> 5;
+    const int sr = swap23 ? ((r & 19) | ((r & 4) << 1) | ((r & 8) >> 1)) : r;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const f32x4 v = {acc[db][4 * i4 + 0] * mul, acc[db][4 * i4 + 1] * mul, acc[db][4 * i4 + 2] * mul,
                          acc[db][4 * i4 + 3] * mul};
-        *reinterpret_cast<bf16x4*>(stage + r * kPitch + (db * 32 + 8 * i4 + 4 * g) * 2) =
+        *reinterpret_cast<bf16x4*>(stage + sr * kPitch + (db * 32 + 8 * i4 + 4 * g) * 2) =
             __builtin_convertvector(v, bf16x4);
       }
     constexpr int kChunks = D / 8;   // 16-byte chunks per row

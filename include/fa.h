@@ -248,6 +248,49 @@ fa_status fa_bwd_phase(int phases, const void* Q, const void* K, const void* V, 
                        int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace fa_bwd_ds needs: the row terms of
+ * fa_bwd_workspace_bytes, then the dS buffer: per (b, h), ceil(Sq/128)
+ * slabs of (Sk rounded up to 128) x 128 bf16 (Sq x Sk x 2 bytes, rounded
+ * up; 512 MiB for B 1, H 16, Sq = Sk = 4096).  0 on invalid sizes or when
+ * one (b, h) slice of the buffer would reach 2^31 bytes (Sq = Sk up to
+ * 32640). */
+size_t fa_bwd_ds_workspace_bytes(int B, int H, int Sq, int Sk, int d, int causal, int deterministic);
+
+/* Backward in the paper's five products per tile pair (S, dP, dV, dK, dQ;
+ * FA4 paper §3.2.1, Eq. 7-8, as summarised on "FlashAttention-4: Algorithm
+ * and Kernel Pipelining Co-Design for Asymmetric Hardware Scaling"), without
+ * its dQ atomics: the kernel that owns a block of keys forms S, dP, P, dS,
+ * dV and dK and also writes dS (rounded to bf16, the operand its dK product
+ * uses) to the workspace; a second kernel forms dQ = scale dS K per block of
+ * 128 query rows.  Inputs, outputs, rounding and arguments as for fa_bwd;
+ * results agree with fa_bwd's to rounding (not bitwise: the summation
+ * orders differ) and are bit-identical run to run in both modes.
+ *   workspace  device memory of at least fa_bwd_ds_workspace_bytes(...);
+ *              contents on entry do not matter; not to be used concurrently
+ *              by another call.
+ * Returns FA_OK, FA_ERR_INVALID (also for a workspace that is too small),
+ * FA_ERR_UNSUPPORTED (also when fa_bwd_ds_workspace_bytes would be 0 for
+ * valid sizes) or FA_ERR_HIP. */
+fa_status fa_bwd_ds(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                    const void* dO, void* dQ, void* dK, void* dV,
+                    int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The three launches of fa_bwd_ds, enqueued separately (the FA_BWD_* bit
+ * mask of fa_bwd_phase, executed in this order within one call):
+ *   FA_BWD_PREPARE  D_i and LSE_i log2(e) into the workspace;
+ *   FA_BWD_DKDV     dK and dV, and dS into the workspace (reads the row
+ *                   terms);
+ *   FA_BWD_DQ       dQ from the workspace's dS and K (writes dQ only).
+ * Each phase reads what the earlier ones wrote into the same workspace, so
+ * separate calls must run in this order (one stream, or events).  Arguments
+ * and validation as for fa_bwd_ds; fa_bwd_ds is
+ * fa_bwd_ds_phase(FA_BWD_ALL, ...). */
+fa_status fa_bwd_ds_phase(int phases, const void* Q, const void* K, const void* V, const void* O,
+                          const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                          int B, int H, int Sq, int Sk, int d, int causal, float scale, int deterministic,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_bwd for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same kernels and results as fa_bwd (bit for bit), with the workspace taken

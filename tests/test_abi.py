@@ -135,6 +135,51 @@ def test_bwd_validation_and_workspace(L):
     assert L.fa_bwd(*bad, ws, vp(0)) == fa.FA_ERR_INVALID
 
 
+def test_bwd_ds_validation_and_workspace(L):
+    """The five-product backward's workspace is the row terms plus one bf16
+    dS^T slab of (Sk rounded up to 128) x 128 per (b, h, block of 128 query
+    rows); it validates like fa_bwd and refuses slices whose dS reaches
+    2^31 bytes."""
+    vp = ctypes.c_void_p
+    rows = fa.fa_bwd_workspace_bytes(2, 3, 300, 200, 64, False, False)
+    ws = fa.fa_bwd_ds_workspace_bytes(2, 3, 300, 200, 64, False, False)
+    assert ws == rows + 2 * 3 * 3 * 256 * 128 * 2
+    assert fa.fa_bwd_ds_workspace_bytes(2, 3, 300, 200, 128, True, True) == ws
+    assert fa.fa_bwd_ds_workspace_bytes(1, 16, 4096, 4096, 128, True, False) == \
+        fa.fa_bwd_workspace_bytes(1, 16, 4096, 4096, 128, True, False) + 16 * 4096 * 4096 * 2
+    assert fa.fa_bwd_ds_workspace_bytes(1, 1, 32640, 32640, 128, True, False) > 0
+    assert fa.fa_bwd_ds_workspace_bytes(1, 1, 32641, 32641, 128, True, False) == 0
+    assert fa.fa_bwd_ds_workspace_bytes(1, 2, 100, 100, 80, True, True) == 0
+    assert fa.fa_bwd_ds_workspace_bytes(0, 2, 100, 100, 64, True, True) == 0
+    ws = fa.fa_bwd_ds_workspace_bytes(1, 2, 100, 100, 64, True, False)
+    args = [vp(FAKE)] * 9 + [1, 2, 100, 100, 64, 1, 0.125, 0, vp(FAKE)]
+    assert L.fa_bwd_ds(*args, ws - 1, vp(0)) == fa.FA_ERR_INVALID
+    for i in (0, 5, 8):
+        bad = list(args)
+        bad[i] = vp(0)
+        assert L.fa_bwd_ds(*bad, ws, vp(0)) == fa.FA_ERR_INVALID
+    bad = list(args)
+    bad[17] = vp(0)                                # null workspace
+    assert L.fa_bwd_ds(*bad, ws, vp(0)) == fa.FA_ERR_INVALID
+    bad = list(args)
+    bad[16] = 2
+    assert L.fa_bwd_ds(*bad, ws, vp(0)) == fa.FA_ERR_INVALID
+    bad = list(args)
+    bad[13] = 96
+    assert L.fa_bwd_ds(*bad, ws, vp(0)) == fa.FA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[12] = 64                                   # causal with Sq != Sk
+    assert L.fa_bwd_ds(*bad, ws, vp(0)) == fa.FA_ERR_UNSUPPORTED
+    big = [vp(FAKE)] * 9 + [1, 1, 32641, 32641, 128, 1, 0.125, 0, vp(FAKE)]
+    assert L.fa_bwd_ds(*big, 1 << 40, vp(0)) == fa.FA_ERR_UNSUPPORTED
+    # the phase entry point: an empty or unknown mask is refused, the rest
+    # validated as above
+    for ph in (0, 8, -1):
+        assert L.fa_bwd_ds_phase(ph, *args, ws, vp(0)) == fa.FA_ERR_INVALID
+    assert L.fa_bwd_ds_phase(fa.FA_BWD_DQ, *args, ws - 1, vp(0)) == fa.FA_ERR_INVALID
+    assert L.fa_bwd_ds_phase(fa.FA_BWD_ALL, *big, 1 << 40, vp(0)) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_realised_emu_share(L):
     assert fa.fa_fwd_realised_emu_frac(128, 0.0) == 0.0
     assert abs(fa.fa_fwd_realised_emu_frac(128, 0.10) - 0.10) < 0.02

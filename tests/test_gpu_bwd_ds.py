@@ -1,0 +1,154 @@
+"""GPU parity of fa_bwd_ds (the five-product backward: dS written by the
+dK/dV kernel, dQ = scale dS K from it) against the CPU oracle, called through
+the C ABI.  As for fa_bwd, the GPU backward consumes the GPU forward's O and
+LSE and the oracle recomputes everything in float64 (max |err| <= 2e-2).
+
+The dK/dV kernel of this form is fa_bwd's with the dS stores added, so dK and
+dV must equal fa_bwd's bit for bit; dQ is summed in another order and must
+agree with fa_bwd's to bf16 rounding."""
+import math
+import sys
+
+import pytest
+import torch
+
+import exact_attention_50_amd as fa
+from oracle import attention_backward
+from parity import check_grads, oracle_backward_heads
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def both(q, k, v, do, causal, det=False, fill=None):
+    """(fa_bwd_ds outputs, fa_bwd outputs) on the GPU forward's O and LSE."""
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal)
+    B, H, Sq, d = q.shape
+    ws = None
+    if fill is not None:
+        n = fa.fa_bwd_ds_workspace_bytes(B, H, Sq, k.shape[2], d, causal, det)
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=DEV)
+    got = fa.backward_ds(qd, kd, vd, o, lse, dod, causal=causal, deterministic=det, workspace=ws)
+    ref = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, deterministic=det)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in got], [t.cpu() for t in ref]
+
+
+def agree_with_split(got, split, what):
+    assert torch.equal(got[1], split[1]), (what, "dK differs from fa_bwd's")
+    assert torch.equal(got[2], split[2]), (what, "dV differs from fa_bwd's")
+    a, b = got[0].double(), split[0].double()
+    # both dQ are fp32 sums of bf16 dS times K, rounded to bf16 once: dS
+    # elements formed in two fp32 orders may round to neighbouring bf16
+    # values, so beside the final rounding (2^-7 relative covers two ulps) a
+    # small share of the tensor's scale is allowed; a misplaced row or key
+    # is off by the scale itself
+    tol = 2.0 ** -7 * b.abs() + 2.0 ** -8 * float(b.abs().max())
+    assert bool(((a - b).abs() <= tol).all()), (what, float((a - b).abs().max()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Sq,Sk,causal", [(1, 1, False), (17, 17, True), (64, 200, False), (128, 128, True),
+                                          (257, 257, True), (200, 333, False), (384, 384, True)])
+def test_small_shapes_every_element(d, Sq, Sk, causal):
+    say(f"bwd_ds small d={d} Sq={Sq} Sk={Sk} causal={causal}")
+    q, k, v, do = make_inputs(2, 2, Sq, Sk, d, seed=Sq * 31 + Sk + d, with_dout=True)
+    got, split = both(q, k, v, do, causal)
+    ref = attention_backward(q, k, v, do, 1 / math.sqrt(d), causal)
+    say(check_grads(got, ref, f"d{d} {Sq}x{Sk} c{causal}"))
+    agree_with_split(got, split, f"d{d} {Sq}x{Sk} c{causal}")
+
+
+@pytest.mark.parametrize("d,Sq,Sk,causal", [(128, 1000, 1000, True), (64, 1000, 1000, True),
+                                            (128, 333, 1100, False), (64, 700, 129, False)])
+def test_ragged_multi_slab_every_element(d, Sq, Sk, causal):
+    """Several 128-row dS slabs, a ragged last slab and key tile."""
+    say(f"bwd_ds ragged d={d} Sq={Sq} Sk={Sk} causal={causal}")
+    q, k, v, do = make_inputs(1, 3, Sq, Sk, d, seed=7 * Sq + Sk + d, with_dout=True)
+    got, split = both(q, k, v, do, causal, det=True)
+    ref = attention_backward(q, k, v, do, 1 / math.sqrt(d), causal)
+    say(check_grads(got, ref, f"d{d} {Sq}x{Sk} c{causal}"))
+    agree_with_split(got, split, f"d{d} {Sq}x{Sk} c{causal}")
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF])
+def test_workspace_contents_do_not_matter(fill):
+    """A workspace of NaN bf16 (0xFFFF) or zeros gives the same bits: the dQ
+    kernel reads only the dS the dK/dV kernel wrote (causal: no slab part
+    above the diagonal)."""
+    say(f"bwd_ds workspace fill {fill:#x}")
+    q, k, v, do = make_inputs(1, 2, 555, 555, 128, seed=77, with_dout=True)
+    a, _ = both(q, k, v, do, True, fill=fill)
+    b, _ = both(q, k, v, do, True, fill=0x7F)
+    for x, y in zip(a, b):
+        assert torch.isfinite(x.float()).all()
+        assert torch.equal(x, y)
+
+
+def test_config5_sampled_heads_and_run_to_run():
+    """The causal B1 H16 S4096 d128 backward: two whole heads against the
+    oracle, dK and dV equal to fa_bwd's, dQ close to it, three runs equal."""
+    w = WORKLOADS[5]
+    say(f"bwd_ds {w.name}")
+    q, k, v, do = workload_inputs(w)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=w.causal)
+    runs = []
+    for _ in range(3):
+        runs.append([t.cpu() for t in fa.backward_ds(qd, kd, vd, o, lse, dod, causal=w.causal)])
+        torch.cuda.synchronize()
+    split = [t.cpu() for t in fa.backward(qd, kd, vd, o, lse, dod, causal=w.causal)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+    agree_with_split(runs[0], split, w.name)
+    heads = [(0, 0), (0, 13)]
+    refs = oracle_backward_heads(q, k, v, do, w.scale, w.causal, heads)
+    for (b, h), ref in zip(heads, refs):
+        g = [t[b:b + 1, h:h + 1] for t in runs[0]]
+        say(h, check_grads(g, ref, f"{w.name} head {h}"))
+    for t in runs[0]:
+        assert torch.isfinite(t.float()).all()
+
+
+def test_non_causal_long_whole_head():
+    """Non-causal B1 H4 S4096 d64: one whole head against the oracle (every
+    key tile of every slab in play), the rest against fa_bwd."""
+    say("bwd_ds non-causal S4096 d64")
+    q, k, v, do = make_inputs(1, 4, 4096, 4096, 64, seed=123, with_dout=True)
+    got, split = both(q, k, v, do, False)
+    agree_with_split(got, split, "non-causal S4096 d64")
+    (ref,) = oracle_backward_heads(q, k, v, do, 1 / 8.0, False, [(0, 2)])
+    say(check_grads([t[:, 2:3] for t in got], ref, "non-causal S4096 d64 head 2"))
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_phases_separately_equal_one_call(d, causal):
+    """fa_bwd_ds_phase(PREPARE), then DKDV, then DQ writes the same bits as
+    one fa_bwd_ds call; PREPARE touches no output, DKDV only dK and dV."""
+    say(f"bwd_ds phases d={d} causal={causal}")
+    q, k, v, do = (t.to(DEV) for t in make_inputs(1, 3, 333, 333, d, seed=60 + d, with_dout=True))
+    o, lse = fa.forward(q, k, v, causal=causal)
+    ref = fa.backward_ds(q, k, v, o, lse, do, causal=causal)
+    nbytes = fa.fa_bwd_ds_workspace_bytes(1, 3, 333, 333, d, causal, False)
+    ws = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    outs = [torch.full_like(q, 7.0) for _ in range(3)]
+    fa.fa_bwd_ds_phase(fa.FA_BWD_PREPARE, q, k, v, o, lse, do, *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    assert all(bool((t == 7.0).all()) for t in outs), "PREPARE wrote an output"
+    fa.fa_bwd_ds_phase(fa.FA_BWD_DKDV, q, k, v, o, lse, do, *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    assert bool((outs[0] == 7.0).all()), "DKDV wrote dQ"
+    assert torch.equal(outs[1], ref[1]) and torch.equal(outs[2], ref[2])
+    fa.fa_bwd_ds_phase(fa.FA_BWD_DQ, q, k, v, o, lse, do, *outs, ws, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
