@@ -65,16 +65,20 @@ struct BwdParams {
 };
 
 // dS^T buffer of the five-product form.  Per (b, h) and block of 128 query
-// rows ("positions", one dQ workgroup each) a slab of 8 groups of 16
-// positions; in group pg, key row k holds positions 16 pg .. +16 as one
-// 32-byte record at byte (pg * ds_rows + k) * 32.  Position 16 x + 8 g + j
-// of a block holds query row 16 x + 8 (j / 4) + 4 g + j % 4 (bits 2 and 3 of
-// the row index exchanged): the order in which a lane of the dK/dV kernel
-// holds dS, so one of its 16-byte stores of a 16-row step covers half a
-// record and a wave's store (32 keys) 1 KB of consecutive records.
+// rows ("positions", one dQ workgroup each) a slab of ds_rows / 64 key tiles
+// of 16 KB: in tile kt, group pg of 16 positions and key k (kt = k / 64)
+// hold positions 16 pg .. +16 of key k as one 32-byte record at byte
+// (kt * 8 + pg) * 2048 + (k % 64) * 32, so the dQ kernel reads each tile as
+// one contiguous block.  Position 16 x + 8 g + j of a block holds query row
+// 16 x + 8 (j / 4) + 4 g + j % 4 (bits 2 and 3 of the row index exchanged):
+// the order in which a lane of the dK/dV kernel holds dS, so one of its
+// 16-byte stores of a 16-row step covers half a record and a wave's store
+// (32 keys) 1 KB of consecutive records.
 constexpr int kDsPositions = 128;
 constexpr int kDsGroup = 16;                                // positions per record
 constexpr int kDsRecord = kDsGroup * 2;                     // bytes per record
+constexpr int kDsTileKeys = 64;                             // keys per slab tile
+constexpr int kDsTileBytes = kDsTileKeys * kDsRecord * (kDsPositions / kDsGroup);   // 16 KB
 
 // ------------------------------------------------------------------- prep
 // D_i and LSE_i log2(e) of every query row into the workspace.
@@ -487,7 +491,8 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   const size_t ds_slab = (size_t)p.ds_rows * kDsPositions;
   const __amdgpu_buffer_rsrc_t rds =
       make_rsrc(DS ? p.ds + (size_t)bh * p.ds_nqb * ds_slab : nullptr, DS ? (unsigned)(p.ds_nqb * ds_slab * 2) : 0u);
-  const int ds_lane = key * kDsRecord + 16 * g;
+  const int ds_lane = (key % kDsTileKeys) * kDsRecord + 16 * g;
+  const int ds_tile = (k0 + wave * kKW) / kDsTileKeys;   // wave-uniform
 
   // B operands: the lane's K and V rows, dims 16 kc + 8 g .. +8
   bf16x8 kf[kKC], vf[kKC];
@@ -627,7 +632,8 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
         constexpr int x = j - (kSteps - 4);
         constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
         const int pg = (q0 % kDsPositions) / kDsGroup + x;
-        const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) + pg * p.ds_rows * kDsRecord;
+        const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) +
+                         (ds_tile * (kDsPositions / kDsGroup) + pg) * (kDsTileBytes / (kDsPositions / kDsGroup));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
       }
       const bf16x8 a = ring[j % kRing];
@@ -734,7 +740,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 // r ^ 4, so the two 16-lane halves of a transposed read pass (groups 2 w and
 // 2 w + 1, same keys) meet opposite halves of the 64 banks.  A tile's loads
 // are spread over its products (a memory-to-LDS load stalls the issuing
-// wave for a while), and each product's operands are read a step ahead.
+// wave for a while), and the K^T operands are read four products ahead (with
+// one product's time between reads the kernel waited on LDS latency: MFMA
+// busy 23 %, LDS active 15 %, and it ran as fast with no tile loads at all).
 // The dS loads carry the non-temporal hint (dS is read once; K stays).
 // Causal: the slab of block qb needs keys 0 .. 128 qb + 127 only (dS is zero
 // past the diagonal, and those are exactly the tiles the dK/dV kernel
@@ -744,8 +752,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;
 constexpr int kStages = 4;
-constexpr int kSBytes = kBN * kDsRecord * (kDsPositions / kDsGroup);   // 16 KB
-constexpr int kSLoads = kSBytes / 1024 / kWaves;                        // per wave
+constexpr int kSlabTiles = kBN / kDsTileKeys;   // slab tiles per key tile
+constexpr int kSBytes = kSlabTiles * kDsTileBytes;
+constexpr int kSLoads = kSBytes / 1024 / kWaves;   // per wave
 template <int D>
 struct Layout {
   static constexpr int kKBytes = kBN * TileGeom<D>::kRowBytes;
@@ -763,6 +772,7 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
   constexpr int kDB = D / 32;
   constexpr int kPer = L::kPer;
   constexpr int kSteps = (kBN / 16) * kDB;   // products per tile and wave
+  constexpr int kAhead = 4;                  // K^T operands in flight
   static_assert(kWaves * 32 == kDsPositions, "one 32-position block per wave");
   static_assert(kPer <= kSteps, "one load per product at most");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -779,22 +789,29 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
   const size_t slab = (size_t)p.ds_rows * kDsPositions;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ds + ((size_t)bh * p.ds_nqb + qb) * slab, (unsigned)(slab * 2));
   const int tr_k = tr_lane_offset<D>(lane);
-  // dS load i of this wave: 1 KB of LDS = records 32 (blk % 2) .. +32 of group
-  // blk / 2, blk = 4 i + w; lane l fetches half l % 2 of record 32 (blk % 2) + l / 2
+  // dS load i of this wave: 1 KB of LDS, blk = i kWaves + w: slab tile
+  // kSlabTiles t + blk / 16, records 32 c .. +32 of its group pg (blk % 16 =
+  // 2 pg + c); lane l fetches half l % 2 of record 32 c + l / 2.  The LDS
+  // copy keeps the slab tiles' layout, one after the other.
+  static_assert(kBN % kDsTileKeys == 0, "whole slab tiles per key tile");
   auto s_src = [&](int t, int i) __attribute__((always_inline)) -> unsigned {
     const int blk = i * kWaves + wave;
-    const int pg = blk >> 1;
-    const int rec = ((blk & 1) * 32 + (lane >> 1)) ^ (4 * (pg & 1));
-    return (unsigned)((pg * p.ds_rows + t * kBN + rec) * kDsRecord + 16 * (lane & 1));
+    const int st = kSlabTiles * t + blk / 16, b16 = blk % 16;
+    const int pg = b16 >> 1;
+    const int rec = ((b16 & 1) * 32 + (lane >> 1)) ^ (4 * (pg & 1));
+    return (unsigned)(st * kDsTileBytes + (pg * kDsTileKeys + rec) * kDsRecord + 16 * (lane & 1));
   };
   // B operand (dS^T, k = keys of step ks in accumulator order, n = position
   // 32 w + lane % 32): two ds_read_b64_tr_b16 over 4 records x 16 positions of
   // group pg = 2 w + h, h = (lane / 16) % 2; rows 16 ks + 4 g + s / 4 (and + 8)
   const int s16 = lane & 15, hh = (lane >> 4) & 1, gg = lane >> 5;
-  const int tr_s = ((2 * wave + hh) * kBN + 4 * (gg ^ hh) + (s16 >> 2)) * kDsRecord + 8 * (s16 & 3);
+  const int tr_s = ((2 * wave + hh) * kDsTileKeys + 4 * (gg ^ hh) + (s16 >> 2)) * kDsRecord + 8 * (s16 & 3);
   auto read_s = [&](const char* stile, int ks) __attribute__((always_inline)) -> bf16x8 {
-    const bf16x4_t lo = lds_read_tr16(stile + tr_s + 16 * ks * kDsRecord);
-    const bf16x4_t hi = lds_read_tr16(stile + tr_s + (16 * ks + 8) * kDsRecord);
+    constexpr int kStepsPerSlabTile = kDsTileKeys / 16;
+    const char* base = stile + (ks / kStepsPerSlabTile) * kDsTileBytes + tr_s;
+    const int kk = ks % kStepsPerSlabTile;
+    const bf16x4_t lo = lds_read_tr16(base + 16 * kk * kDsRecord);
+    const bf16x4_t hi = lds_read_tr16(base + (16 * kk + 8) * kDsRecord);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   auto load_one = [&](int t, int i) __attribute__((always_inline)) {
@@ -830,25 +847,25 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     const char* kt = smem + (t % kStages) * L::kStageBytes;
     const char* stile = kt + L::kKBytes;
     const bool more = t + kLead < n;
-    bf16x8 a_cur = read_cols<D>(kt, tr_k, 0, 0);
-    bf16x8 b_cur = read_s(stile, 0);
+    // operands read kAhead products ahead (an LDS read takes several products'
+    // time to return); the tile's four dS operands right after the barrier
+    bf16x8 b[kBN / 16];
+    bf16x8 a[kAhead];
+    static_for<kBN / 16>([&](auto KS) __attribute__((always_inline)) { b[KS] = read_s(stile, KS); });
+    static_for<kAhead>([&](auto J) __attribute__((always_inline)) {
+      a[J] = read_cols<D>(kt, tr_k, J / kDB, J % kDB);
+    });
     static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
       constexpr int j = J;
       constexpr int ks = j / kDB, db = j % kDB;
-      bf16x8 a_nxt = a_cur, b_nxt = b_cur;
-      if constexpr (j + 1 < kSteps) {
-        a_nxt = read_cols<D>(kt, tr_k, (j + 1) / kDB, (j + 1) % kDB);
-        if constexpr ((j + 1) % kDB == 0) b_nxt = read_s(stile, (j + 1) / kDB);
-      }
+      const bf16x8 a_j = a[j % kAhead];
+      if constexpr (j + kAhead < kSteps) a[j % kAhead] = read_cols<D>(kt, tr_k, (j + kAhead) / kDB, (j + kAhead) % kDB);
       constexpr int every = kSteps / kPer;
       if constexpr (j % every == 0 && j / every < kPer) {
         if (more) load_one(t + kLead, j / every);
       }
-      acc[db] = mfma32x32x16(a_cur, b_cur, acc[db]);
+      acc[db] = mfma32x32x16(a_j, b[ks], acc[db]);
       __builtin_amdgcn_sched_barrier(0);
-      a_cur = a_nxt;
-      b_cur = b_nxt;
-      (void)ks;
     });
   }
 
