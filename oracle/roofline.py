@@ -32,7 +32,8 @@ instruction on one SIMD, enough independent work to reach throughput):
     per clock per CU (half of each with 4 wavefronts: the reads are latency
     bound below 8 wavefronts);
   * an MFMA wavefront and a VALU wavefront sharing a SIMD both keep their own
-    rate (32.0 and 6.2 cycles), so matrix and vector work overlap.
+    rate (32.0 and 6.2 cycles), so matrix and vector work overlap;
+  * HBM: the published 8 TB/s, 13.02 bytes per clock per CU at 2.4 GHz.
 On CDNA4 Q stays in registers (the B operand of S^T = K Q^T); every
 wavefront of ``rows_per_wave`` query rows reads the whole K tile row-wise and
 the V tile transposed from LDS.
@@ -46,7 +47,13 @@ MI355X_CU = dict(name="MI355X CU", mma_flops_per_clk=4096.0, clock_hz=2.4e9, n_c
                  valu_cycles=4.3,             # fp32 VALU instruction (wave64), per SIMD
                  exp_cycles=9.1,              # v_exp_f32 (wave64), per SIMD
                  lds_row_bytes_per_clk=213.0,     # ds_read_b128, per CU
-                 lds_tr_bytes_per_clk=128.0)      # ds_read_b64_tr_b16, per CU
+                 lds_tr_bytes_per_clk=128.0,      # ds_read_b64_tr_b16, per CU
+                 hbm_bytes_per_s=8.0e12)          # published HBM3E bandwidth, whole chip
+
+
+def hbm_bytes_per_clk(hw=MI355X_CU):
+    """One CU's share of the HBM bandwidth per clock at the nominal clock."""
+    return hw["hbm_bytes_per_s"] / hw["n_cu"] / hw["clock_hz"]
 
 
 def forward_tile_cycles_b200(M, N, d, hw=B200_SM, qtile_rows=128, elem_bytes=2):
@@ -93,27 +100,52 @@ def forward_tile_cycles_cdna4(M, N, d, rows_per_wave=32, valu_per_score=3.2, row
 
 
 def gradient_tile_cycles_cdna4(M_own, N_stream, d, products, row_reads, tr_reads, valu_per_elem=6.0,
-                               hw=MI355X_CU, elem_bytes=2):
+                               hw=MI355X_CU, elem_bytes=2, ds_store=False):
     """CU cycles of each unit for one tile of a gradient kernel: a workgroup
     owning M_own rows (keys for dK/dV, queries for dQ) against N_stream
     streamed rows, with ``products`` matrix products of 2 M N d FLOPs each
     (4 for dK/dV: S, dP, dV, dK; 3 for dQ: S, dP, dQ), one exponential and
     valu_per_elem other VALU instructions per (own, streamed) pair, and
     row_reads / tr_reads streamed-tile reads per wavefront of 32 own rows
-    (row-wise and transposed: Q, dO / K, V read as each kind of operand)."""
+    (row-wise and transposed: Q, dO / K, V read as each kind of operand).
+    ds_store (the dK/dV kernel of the five-product form): the tile's dS,
+    M N bf16 values, is written to HBM -- hbm = those bytes at the CU's
+    share of the HBM bandwidth (the streamed tiles come from L2)."""
     mma = 2.0 * products * M_own * N_stream * d / hw["mma_flops_per_clk"]
     exp = _per_cu(M_own * N_stream / 64, hw["exp_cycles"], hw)
     valu = _per_cu(valu_per_elem * M_own * N_stream / 64, hw["valu_cycles"], hw)
     tile_bytes = (M_own / 32) * N_stream * d * elem_bytes
     lds = (row_reads * tile_bytes / hw["lds_row_bytes_per_clk"]
            + tr_reads * tile_bytes / hw["lds_tr_bytes_per_clk"])
-    return dict(mma=mma, exp=exp, valu=valu, issue=exp + valu, lds=lds)
+    c = dict(mma=mma, exp=exp, valu=valu, issue=exp + valu, lds=lds)
+    if ds_store:
+        c["hbm"] = M_own * N_stream * 2 / hbm_bytes_per_clk(hw)
+    return c
+
+
+def ds_product_tile_cycles_cdna4(M_own, N_stream, d, waves=4, hw=MI355X_CU):
+    """CU cycles of each unit for one tile of the dQ = dS K kernel of the
+    five-product form: a workgroup of ``waves`` wavefronts owning M_own query
+    rows (32 per wavefront) against N_stream keys.  mma = one product,
+    2 M N d FLOPs; lds = every wavefront reads the K tile transposed
+    (N d bf16) and its 32 columns of the dS tile transposed (N x 32 bf16),
+    at the transposed-read rate, halved below 8 wavefronts per CU (the reads
+    are latency bound there); hbm = the dS tile, M N bf16 values, streamed
+    from HBM once (K is re-read from L2); no exponentials, no VALU work to
+    speak of."""
+    mma = 2.0 * M_own * N_stream * d / hw["mma_flops_per_clk"]
+    tr_bytes = (M_own / 32) * (N_stream * d + N_stream * 32) * 2
+    rate = hw["lds_tr_bytes_per_clk"] * (1.0 if waves >= 8 else 0.5)
+    lds = tr_bytes / rate
+    hbm = M_own * N_stream * 2 / hbm_bytes_per_clk(hw)
+    return dict(mma=mma, exp=0.0, valu=0.0, issue=0.0, lds=lds, hbm=hbm)
 
 
 def bound(cycles):
-    """The unit with the most cycles among mma, issue and lds (and its share
-    of the tile time for every unit: predicted busy fractions)."""
-    units = {k: cycles[k] for k in ("mma", "issue", "lds")}
+    """The unit with the most cycles among mma, issue, lds (and hbm where
+    the tile has HBM traffic of its own), and each unit's share of the tile
+    time (predicted busy fractions)."""
+    units = {k: cycles[k] for k in ("mma", "issue", "lds", "hbm") if k in cycles}
     name = max(units, key=units.get)
     top = units[name]
     return name, {k: v / top for k, v in units.items()}

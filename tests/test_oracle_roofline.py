@@ -83,3 +83,27 @@ def test_cdna4_model_at_b200_rates_is_table1():
     b200_like = dict(roofline.MI355X_CU, mma_flops_per_clk=8192.0, simds=1, exp_cycles=64 / 16.0)
     c = roofline.forward_tile_cycles_cdna4(256, 128, 128, row_sum_mfma=False, hw=b200_like)
     assert c["mma"] == 2048.0 and c["exp"] == 2048.0
+
+
+def test_cdna4_hbm_terms_hand_derived():
+    """HBM share per CU: 8e12 / 256 / 2.4e9 = 13.0208 bytes per clock.  dK/dV
+    tile of the five-product form writes its dS, 128 x 64 x 2 = 16384 bytes:
+    16384 / 13.0208 = 1258.29 cycles, below the 2048 of its products.  The
+    dQ = dS K tile (128 query rows, 64 keys, d = 128, 4 waves): mma =
+    2*128*64*128/4096 = 512; LDS = 4 waves x (64 x 128 + 64 x 32) x 2 bytes
+    = 81920 bytes at half of 128 B/clk = 1280; hbm = 16384 / 13.0208 =
+    1258.29: bound by LDS, HBM within 2 %, the products at 40 %.  With 8
+    waves the LDS term halves and HBM bounds."""
+    assert _close(roofline.hbm_bytes_per_clk(), 8e12 / 256 / 2.4e9)
+    g = roofline.gradient_tile_cycles_cdna4(128, 64, 128, products=4, row_reads=2, tr_reads=2, ds_store=True)
+    assert _close(g["hbm"], 16384 * 256 * 2.4e9 / 8e12) and _close(g["mma"], 2048.0)
+    assert roofline.bound(g)[0] == "mma"
+    assert "hbm" not in roofline.gradient_tile_cycles_cdna4(128, 64, 128, products=4, row_reads=2, tr_reads=2)
+    c = roofline.ds_product_tile_cycles_cdna4(128, 64, 128)
+    assert _close(c["mma"], 512.0) and _close(c["lds"], 1280.0) and _close(c["hbm"], 1258.2912)
+    name, frac = roofline.bound(c)
+    assert name == "lds" and _close(frac["mma"], 0.4) and _close(frac["hbm"], 1258.2912 / 1280.0)
+    c8 = roofline.ds_product_tile_cycles_cdna4(128, 64, 128, waves=8)
+    assert _close(c8["lds"], 640.0) and roofline.bound(c8)[0] == "hbm"
+    c64 = roofline.ds_product_tile_cycles_cdna4(128, 64, 64)
+    assert _close(c64["mma"], 256.0) and _close(c64["lds"], 4 * (64 * 64 + 64 * 32) * 2 / 64.0)
