@@ -32,10 +32,10 @@
 //     A operand is read from row-major V in LDS with ds_read_b64_tr_b16;
 //   * K / V tiles with the chunk permutation of fa_tiles.hpp (bank-conflict-
 //     free operand reads): the 256-row form streams 128-key tiles through a
-//     2-stage K ring and a 2-stage V ring, loaded memory-to-LDS two intervals
-//     ahead of their first read; the split form streams 64-key tiles through
-//     a 4-stage K+V ring, staged through registers; buffer descriptors bound
-//     every head, so rows past the end read zeros;
+//     2-stage K ring and a 2-stage V ring, the split form 64-key tiles
+//     through a 5-stage K+V ring, both loaded memory-to-LDS two intervals
+//     ahead of their first read; buffer descriptors bound every head, so rows
+//     past the end read zeros;
 //   * the bf16 output leaves through a per-wave LDS area as whole rows.
 
 #include <type_traits>
@@ -52,10 +52,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;               // query rows per wavefront
 constexpr int kBM = kWaves * kQW;     // query rows per workgroup
 // keys per tile: 128 in the 256-row form (two 2-stage rings, K and V), 64 in
-// the split form (one 4-stage ring of K+V stages)
+// the split form (one 5-stage ring of K+V stages)
 constexpr int kBNFull = 128;
 constexpr int kBNSplit = 64;
-constexpr int kStages = 4;            // split form
+constexpr int kStages = 5;            // split form (5 x 32 KB = all 160 KB of LDS at d = 128)
 
 struct FwdParams {
   const bf16* q;
@@ -76,8 +76,8 @@ struct FwdParams {
 };
 
 // LDS of the 256-row form: K ring of 2 stages, then V ring of 2 stages, each
-// stage one 128-key tile.  Split form: 4 stages of (K tile, V tile) of 64
-// keys.  Both take 4 * 128 * 2D bytes (128 KiB at D = 128).
+// stage one 128-key tile: 4 * 128 * 2D bytes (128 KiB at D = 128).  Split
+// form: 5 stages of (K tile, V tile) of 64 keys (160 KiB at D = 128).
 template <int D, bool SPLIT>
 struct FwdLayout {
   static constexpr int kBN = SPLIT ? kBNSplit : kBNFull;
@@ -85,10 +85,10 @@ struct FwdLayout {
   static constexpr int kTileBytes = kBN * kRowBytes;
   static constexpr int kLdsBytes = SPLIT ? kStages * 2 * kTileBytes : 4 * kTileBytes;
   __device__ __forceinline__ static char* k_stage(char* smem, int u) {
-    return SPLIT ? smem + (u & (kStages - 1)) * 2 * kTileBytes : smem + (u & 1) * kTileBytes;
+    return SPLIT ? smem + (u % kStages) * 2 * kTileBytes : smem + (u & 1) * kTileBytes;
   }
   __device__ __forceinline__ static char* v_stage(char* smem, int u) {
-    return SPLIT ? smem + (u & (kStages - 1)) * 2 * kTileBytes + kTileBytes : smem + (2 + (u & 1)) * kTileBytes;
+    return SPLIT ? smem + (u % kStages) * 2 * kTileBytes + kTileBytes : smem + (2 + (u & 1)) * kTileBytes;
   }
 };
 
@@ -307,27 +307,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // interval 2u-2) and V_u replaces V_{u-2} (last read in 2u), so interval
   // 2u-1 issues K_u and V_{u-1} (fetch(u)) and the end of interval 2u waits
   // for them (commit): every load has two intervals to arrive.  The split
-  // form writes tile k+1's stage in the interval right after tile k-3's last
-  // read; it stages tiles through registers (fetch one interval ahead, write
-  // to LDS at the start of the next), so the global load gets a whole
-  // interval without a fifth stage.  It fetches and writes unconditionally:
-  // past the last tile that costs a little bandwidth (rows past the head
-  // read as zeros) and saves the register copies a conditional load needs.
-  TileIO<D, kBN, kWaves> kio, vio;
+  // form loads tile u (K and V, one 5-stage ring) memory-to-LDS at the start
+  // of interval u-1, into the stage of tile u-5, whose last read was in
+  // interval u-2, and waits for it at the end of interval u: two intervals
+  // for every load too (staged through registers with four stages, the load
+  // had one).  It fetches unconditionally: past the last tile that costs a
+  // little bandwidth (rows past the head read as zeros) and keeps the
+  // per-wave load count, which the waits count, the same every interval.
   using DMA = TileDMA<D, kBN, kWaves>;
+  constexpr int kSplitLoads = 2 * DMA::kLoads;   // per wave and tile (K, V)
   auto fetch = [&](int u) __attribute__((always_inline)) {
     if constexpr (SPLIT) {
-      kio.fetch(rk, u * kBN, wave, lane);
-      vio.fetch(rv, u * kBN, wave, lane);
+      DMA::load(rk, u * kBN, L::k_stage(smem, u), wave, lane);
+      DMA::load(rv, u * kBN, L::v_stage(smem, u), wave, lane);
     } else {
       if (u < n) DMA::load(rk, u * kBN, L::k_stage(smem, u), wave, lane);
       if (u >= 1 && u <= n) DMA::load(rv, (u - 1) * kBN, L::v_stage(smem, u - 1), wave, lane);
     }
   };
-  auto commit = [&](int u) __attribute__((always_inline)) {
+  // 256-row form: every load issued so far; split form: all but the last
+  // tile's (the one fetched in this interval)
+  auto commit = [&](int) __attribute__((always_inline)) {
     if constexpr (SPLIT) {
-      kio.store(L::k_stage(smem, u), wave, lane);
-      vio.store(L::v_stage(smem, u), wave, lane);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSplitLoads) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -340,22 +342,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
   if constexpr (SPLIT) {
     // Interval k = 1 .. max(n, 2) + 2, one workgroup barrier after each.  Every wave
-    // opens interval k by writing tile k (fetched during interval k-1) to
-    // stage k % 4 and fetching tile k+1, so tile u is readable from interval
-    // u+1.  Group g takes the tiles u = 2t + g: matrix(t) in interval 2t+1+g
-    // (S of tile u, P V of tile u-2) and vector(t) one interval later.  The
-    // last read of tile u (its V) falls in interval u+3, before tile u+4
-    // replaces it in interval u+4.
+    // opens interval k by loading tile k+1 into stage (k+1) % 5 and closes it
+    // by waiting for tile k (all but tile k+1's loads), so tile u is readable
+    // from interval u+1.  Group g takes the tiles u = 2t + g: matrix(t) in
+    // interval 2t+1+g (S of tile u, P V of tile u-2) and vector(t) one
+    // interval later.  The last read of tile u (its V) falls in interval
+    // u+3, before tile u+5's load in interval u+4.
     fetch(0);
-    commit(0);
     fetch(1);
+    commit(0);
     barrier();
     int k = 1;
-    auto open = [&]() __attribute__((always_inline)) {
-      commit(k);
-      fetch(k + 1);
-    };
+    auto open = [&]() __attribute__((always_inline)) { fetch(k + 1); };
     auto close = [&]() __attribute__((always_inline)) {
+      commit(k);
       barrier();
       ++k;
     };
@@ -478,7 +478,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   }
   if constexpr (SPLIT) {
     // group 1 hands (O, row sums, reference max) of each lane to the lane of
-    // group 0 that holds the same row and columns; the ring is idle now
+    // group 0 that holds the same row and columns, in the ring: once every
+    // wave's last tile load (issued in the last interval, past the last
+    // tile) has landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
     constexpr int kXO = kDB * 4 * 256 * 16;   // O: [db * 4 + i4][256 lanes] f32x4
     static_assert(kXO + 3 * 256 * 4 <= L::kLdsBytes, "merge area exceeds the LDS ring");
     const int tl = (wave & 3) * 64 + lane;
