@@ -799,6 +799,12 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     const int st = kSlabTiles * t + blk / 16, b16 = blk % 16;
     const int pg = b16 >> 1;
     const int rec = ((b16 & 1) * 32 + (lane >> 1)) ^ (4 * (pg & 1));
+    // a key past Sk (the zero-padded end of the last key block) gets an
+    // offset past the buffer's end (2^31: beyond every slab, no 32-bit wrap),
+    // so the load writes zeros: its dS, formed from zero K and V rows as
+    // P = exp(-LSE) times (0 - D), need not be finite, and times its zero K
+    // row would make dQ NaN
+    if (st * kDsTileKeys + rec >= p.Sk) return 0x80000000u;
     return (unsigned)(st * kDsTileBytes + (pg * kDsTileKeys + rec) * kDsRecord + 16 * (lane & 1));
   };
   // B operand (dS^T, k = keys of step ks in accumulator order, n = position

@@ -152,3 +152,29 @@ def test_phases_separately_equal_one_call(d, causal):
     torch.cuda.synchronize()
     for a, b in zip(outs, ref):
         assert torch.equal(a, b)
+
+
+def test_keys_past_sk_with_very_negative_scores():
+    """Non-causal, Sk = 200 (the last 128-key block has 56 keys past Sk, read
+    as zero rows), every score about -141 (LSE about -136): a key past Sk
+    would have P = exp(0 - LSE) = inf.  Its dS must not reach dQ (inf times
+    its zero K row is NaN): every gradient finite (on a NaN-filled
+    workspace), dK and dV equal to the split form's, dQ equal to it to
+    rounding, all within the gradient tolerance of the oracle.  (dQ is a
+    cancellation of K's large common component here, about 2e-3, so its
+    error relative to its own size is a few percent in both forms.)"""
+    say("bwd_ds keys past Sk, scores about -141")
+    B, H, Sq, Sk, d = 1, 2, 130, 200, 128
+    g = torch.Generator().manual_seed(7)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = (40.0 * u + 0.3 * torch.randn(B, H, Sq, d, generator=g)).to(torch.bfloat16)
+    k = (-40.0 * u + 0.3 * torch.randn(B, H, Sk, d, generator=g)).to(torch.bfloat16)
+    v = (0.1 * torch.randn(B, H, Sk, d, generator=g)).to(torch.bfloat16)
+    do = (0.1 * torch.randn(B, H, Sq, d, generator=g)).to(torch.bfloat16)
+    got, split = both(q, k, v, do, False, fill=0xFF)
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    agree_with_split(got, split, "keys past Sk")
+    ref = attention_backward(q, k, v, do, 1 / math.sqrt(d), False)
+    say(check_grads(got, ref, "keys past Sk"))
