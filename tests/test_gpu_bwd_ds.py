@@ -9,6 +9,7 @@ agree with fa_bwd's to bf16 rounding."""
 import math
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -178,3 +179,32 @@ def test_keys_past_sk_with_very_negative_scores():
     agree_with_split(got, split, "keys past Sk")
     ref = attention_backward(q, k, v, do, 1 / math.sqrt(d), False)
     say(check_grads(got, ref, "keys past Sk"))
+
+
+def test_largest_slice_sampled():
+    """Causal B1 H1 Sq = Sk = 32640, d = 64: one (b, h) slice of dS is just
+    under 2^31 bytes, the largest fa_bwd_ds accepts (32-bit offsets at their
+    limit).  dK and dV must equal the split form's bit for bit; dQ rows
+    (each depends on its own row only) are checked against the oracle on
+    sampled rows, including the first and last."""
+    S, d = 32640, 64
+    say(f"bwd_ds largest slice S={S} d={d}")
+    assert fa.fa_bwd_ds_workspace_bytes(1, 1, S, S, d, True, False) > 0
+    assert fa.fa_bwd_ds_workspace_bytes(1, 1, S + 1, S + 1, d, True, False) == 0
+    q, k, v, do = make_inputs(1, 1, S, S, d, seed=171, with_dout=True)
+    got, split = both(q, k, v, do, True)
+    assert torch.equal(got[1], split[1]) and torch.equal(got[2], split[2])
+    for t in got:
+        assert torch.isfinite(t.float()).all()
+    rng = np.random.default_rng(171)
+    rows = sorted(set(rng.choice(S, size=12, replace=False).tolist()) | {0, 1, 127, 128, S - 1})
+    scale = 1 / math.sqrt(d)
+    worst = 0.0
+    for i in rows:
+        sl = lambda t, n: t[:, :, :n].double().numpy()                      # noqa: E731
+        qi = lambda t: t[:, :, i:i + 1].double().numpy()                     # noqa: E731
+        ref = attention_backward(qi(q), sl(k, i + 1), sl(v, i + 1), qi(do), scale, False)
+        err = float(np.abs(got[0][:, :, i:i + 1].double().numpy() - ref[0]).max())
+        worst = max(worst, err)
+        assert err <= 2e-2, (i, err)
+    say(f"{len(rows)} sampled dQ rows, worst {worst:.3g}")
