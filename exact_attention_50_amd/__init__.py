@@ -14,10 +14,13 @@ import math
 import os
 
 __all__ = [
-    "FAError", "lib", "fa_fwd", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
-    "fa_exp2_probe", "fa_status_str", "fa_fwd_realised_emu_frac", "forward", "forward_partial", "merge",
-    "backward", "fa_bwd_noalloc", "fa_bwd_ds", "fa_bwd_ds_phase", "fa_bwd_ds_workspace_bytes", "backward_ds", "fa_fwd_mxfp4", "forward_mxfp4", "fa_fwd_fp8_blocks", "forward_fp8_blocks",
-    "LIB_PATH",
+    "FAError", "lib", "LIB_PATH", "fa_status_str",
+    "fa_fwd", "fa_fwd_realised_emu_frac", "fa_fwd_rescale_count", "fa_fwd_partial", "fa_merge", "fa_exp2_probe",
+    "fa_fwd_fp8", "fa_fwd_fp8_blocks", "fa_fwd_mxfp4",
+    "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes", "fa_bwd_noalloc",
+    "fa_bwd_ds", "fa_bwd_ds_phase", "fa_bwd_ds_workspace_bytes",
+    "forward", "forward_partial", "merge", "forward_fp8", "forward_fp8_blocks", "forward_mxfp4",
+    "backward", "backward_ds",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")

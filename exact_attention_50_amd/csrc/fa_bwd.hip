@@ -9,19 +9,21 @@
 //
 // CDNA4 design (ours).  The paper adds every key block's dQ contribution with
 // atomics (and orders them behind a lock in its deterministic mode).  On
-// MI355X fp32 atomics to one accumulator from many XCDs run at ~1 TB/s, and
-// ordering them serialises the key blocks of a head.  Here the backward is
-// split by output instead, so every output element is written exactly once:
+// MI355X the float32 atomic adds of that pattern run at ~1.3 TB/s (measured,
+// probes/dq_atomics.hip), and ordering them serialises the key blocks of a
+// head.  Here the backward is split by output instead, so every output
+// element is written exactly once:
 //   bwd_prep_kernel   D_i (inside bwd_dq_kernel when both run in one call);
-//   bwd_dq_kernel     a workgroup owns 256 query rows and streams K / V tiles:
+//   bwd_dq_kernel     a workgroup owns 128 query rows and streams K / V tiles:
 //                     S^T = K Q^T, dP^T = V dO^T (one query per lane, so LSE_i
 //                     and D_i are per-lane scalars), dS^T, dQ^T += K^T dS^T;
 //   bwd_dkdv_kernel   a workgroup owns 128 key rows and streams Q / dO tiles:
 //                     S = Q K^T, dP = dO V^T (one key per lane), P, dS,
 //                     dV^T += dO^T P, dK^T += Q^T dS.
 // That is seven products per tile pair instead of five, no atomics, no
-// workspace beyond the row terms D and LSE log2(e), and results that are bit-identical run to run in both
-// modes (the deterministic flag costs nothing).  Tiles use the layout of
+// workspace beyond the row terms D and LSE log2(e), and results that are
+// bit-identical run to run in both modes (the deterministic flag costs
+// nothing).  Tiles use the layout of
 // fa_tiles.hpp, so Q, dO, K and V are each read both row-wise and transposed
 // from one LDS copy.
 //

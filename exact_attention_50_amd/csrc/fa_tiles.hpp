@@ -71,44 +71,15 @@ __device__ __forceinline__ bf16x8 read_cols(const char* tile, int tr_lane, int k
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Wave-wide bounds-checked fetch of a tile's share into registers and its
-// store into LDS with the chunk permutation.  ROWS rows are split over NW
-// waves; wave `wave` handles loads i = 0 .. kLoads-1 (rows of load (i NW +
-// wave)).  Rows at or past the descriptor's end read as zeros.
-template <int D, int ROWS, int NW>
-struct TileIO {
-  static constexpr int kLoads = ROWS / TileGeom<D>::kRowsPerLoad / NW;
-  static_assert(kLoads >= 1, "tile too small for the workgroup");
-  u32x4 r[kLoads];
-
-  __device__ __forceinline__ void fetch_one(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane, int i) {
-    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
-    const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
-    r[i] = load16(src, (unsigned)(row0 + row) * TileGeom<D>::kRowBytes + (lane % TileGeom<D>::kChunks) * 16);
-  }
-  __device__ __forceinline__ void store_one(char* tile, int wave, int lane, int i) const {
-    constexpr int RPL = TileGeom<D>::kRowsPerLoad;
-    const int row = (i * NW + wave) * RPL + lane / TileGeom<D>::kChunks;
-    const int c = lane % TileGeom<D>::kChunks;
-    *reinterpret_cast<u32x4*>(tile + row * TileGeom<D>::kRowBytes + ((c ^ tile_swz<D>(row)) * 16)) = r[i];
-  }
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t src, int row0, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) fetch_one(src, row0, wave, lane, i);
-  }
-  __device__ __forceinline__ void store(char* tile, int wave, int lane) const {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) store_one(tile, wave, lane, i);
-  }
-};
-
-// The same tile share loaded straight from memory into LDS (gfx950's
-// 16-byte buffer_load ... lds).  One such load writes 64 x 16 contiguous LDS
-// bytes, lane i at the uniform base + 16 i, i.e. RowsPerLoad whole rows; so
-// lane i fetches the global chunk that belongs at its LDS position: chunk
+// A tile's share (ROWS rows split over NW waves; wave `wave` handles loads
+// i = 0 .. kLoads-1, the rows of load i NW + wave) loaded straight from
+// memory into LDS with the chunk permutation (gfx950's 16-byte
+// buffer_load ... lds).  One such load writes 64 x 16 contiguous LDS bytes,
+// lane i at the uniform base + 16 i, i.e. RowsPerLoad whole rows; so lane i
+// fetches the global chunk that belongs at its LDS position: chunk
 // (i % Chunks) ^ f(row) of the row.  Rows at or past the descriptor's end
 // are written as zeros.  The writes complete with the wave's vector-memory
-// counter: wait for vmcnt(0), then a barrier, before other waves read them.
+// counter: wait for vmcnt, then a barrier, before other waves read them.
 template <int D, int ROWS, int NW>
 struct TileDMA {
   static constexpr int kLoads = ROWS / TileGeom<D>::kRowsPerLoad / NW;
