@@ -409,31 +409,58 @@ __global__ __launch_bounds__(dqk::kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // =================================================================== dK dV
-// 4 wavefronts x 32 keys = 128 keys per workgroup (one wave per SIMD); query
-// tiles of 64 rows.  Per tile a wave runs one fixed sequence of kSteps MFMAs,
-//   [S, dP of rows 0-31] [S, dP of rows 32-63] [dV, dK of rows 0-31] [... 32-63]
-// whose LDS operands stream through a ring of kRing registers that runs on
-// across tiles, and whose P / dS arithmetic is spread element by element over
-// the MFMAs of the following block.  Tiles arrive memory-to-LDS in a 3-stage
-// ring, issued two tiles ahead; the one barrier per tile sits kRing steps
-// before the tile's end, once every operand of the tile has been read.
+// 8 wavefronts, two on every SIMD, for 128 keys (four blocks of 32 keys);
+// query tiles of 64 rows.  The two waves of a SIMD share a 32-key block and
+// split each tile's work between them:
+//   S wave  (wave w < 4):  S = Q K^T, P = 2^(scale log2(e) S - LSE log2(e))
+//                          (causal mask applied), dV^T += dO^T P;
+//   dP wave (wave w + 4):  dP = dO V^T, dS = P (dP - D) with P taken from
+//                          the S wave through LDS in float32, dK^T += Q^T dS.
+// They take turns on the matrix unit, one tile pipelined over two phases:
+//   phase A(k)  S wave: dV^T += dO(k)^T P(k), S(k+1) = Q(k+1) K^T   (MFMA)
+//               dP wave: dS(k) from P(k), dP(k)                     (VALU)
+//   phase B(k)  dP wave: dK^T += Q(k)^T dS(k), dP(k+1) = dO(k+1) V^T (MFMA)
+//               S wave: P(k+1) from S(k+1), written to LDS          (VALU)
+// so in every phase one wave of a SIMD issues only products (operands
+// streamed from LDS through a register ring that runs on across phases) and
+// the other only element work, with a barrier between phases.  A prelude
+// forms S(0), P(0) and dP(0); the last interval forms S(n), P(n), dP(n) of
+// a tile that does not exist (LDS contents never used, every address in the
+// allocation) so that all intervals run the same code.
+// Tiles arrive memory-to-LDS in a 3-stage ring (tiles k and k + 1 are read
+// during interval k): the loads of tile k + 2 are issued at the start of
+// A(k) and published at the barrier after B(k).
 namespace kvk {
-constexpr int kWaves = 4;
+constexpr int kPairs = 4;                // 32-key blocks per workgroup
+constexpr int kWaves = 2 * kPairs;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKW = 32;
-constexpr int kBK = kWaves * kKW;
+constexpr int kBK = kPairs * kKW;
 constexpr int kBQ = 64;
 constexpr int kStages = 3;
-constexpr int kRing = 8;
+// LDS by kind: the Q tiles of the stages, then the dO tiles, so that every
+// operand read of a wave (Q and dO only) is a lane address plus an
+// immediate offset below 64 KB from its kind's base; then per stage the
+// tile's 64 rows of LSE log2(e) and of D; then P of each pair, float32 in
+// the S wave's accumulator order: block b, elements 4 i4 .. 4 i4 + 3 of
+// lane l at ((4 b + i4) 64 + l) 16.
 template <int D>
 struct Layout {
   static constexpr int kTileBytes = kBQ * TileGeom<D>::kRowBytes;
-  // Q, dO, then four 64-float row blocks: LSE*log2e, D (waves 0, 1) and the
-  // same again (waves 2, 3 load a copy so every wave issues the same loads)
-  static constexpr int kRowsOff = 2 * kTileBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes + 4 * kBQ * 4;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kLoadsPerTile = 2 * TileDMA<D, kBQ, kWaves>::kLoads + 1;   // per wave
+  static constexpr int kQOff = 0;
+  static constexpr int kDoOff = (kStages * kTileBytes + 16383) / 16384 * 16384;
+  static constexpr int kRowsOff = kDoOff + kStages * kTileBytes;
+  static constexpr int kRowsBytes = 2 * kBQ * 4;   // per stage
+  static constexpr int kPOff = kRowsOff + kStages * kRowsBytes;
+  static constexpr int kPPairBytes = kKW * kBQ * 4;
+  static constexpr int kLdsBytes = kPOff + kPairs * kPPairBytes;
+  // the dP waves load the tiles: kTileLoads per wave and tile, plus one
+  // row-term load for the waves of pairs 0 (LSE) and 1 (D)
+  static constexpr int kTileLoads = 2 * TileDMA<D, kBQ, kPairs>::kLoads;
+  // a kind's base shares no bit with a lane offset within a tile (nor with
+  // the constants those are XORed with), and its tiles span under 64 KB
+  static_assert(kQOff == 0 && kDoOff % 16384 == 0 && kTileBytes <= 16384, "tile kinds' bases");
+  static_assert(kStages * kTileBytes <= 65536, "a kind's tiles span more than 64 KB");
 };
 }  // namespace kvk
 
@@ -443,80 +470,40 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   using namespace kvk;
   using L = Layout<D>;
   using G = TileGeom<D>;
-  constexpr int kKC = D / 16;               // 16-dim steps of S and dP
-  constexpr int kDB = D / 32;               // 32-dim blocks of dK^T / dV^T
-  constexpr int kNS = 2 * kKC;              // MFMAs of S and dP per 32-row block
-  constexpr int kND = 2 * kDB;              // MFMAs of dV and dK per 16-row step
-  constexpr int kSteps = 2 * kNS + 4 * kND;
-  constexpr int kBar = kSteps - kRing;      // barrier position (before this step)
-  // operand j of any tile sits in ring slot j % kRing only if every tile
-  // starts on slot 0
-  static_assert(kSteps % kRing == 0, "ring must divide the step count");
-  constexpr int kPPS = D == 128 ? 1 : 2;    // P/dS elements per step
-  constexpr int kPer = L::kLoadsPerTile;
-  // the row terms of both blocks are read before the barrier frees the stage,
-  // and every bf16 P / dS half is packed before its first dV / dK product
-  static_assert(2 * kNS + 2 + 12 / kPPS - 3 < kBar, "row terms read after the barrier");
-  static_assert(kNS + 2 + 7 / kPPS < 2 * kNS && kNS + 2 + 15 / kPPS < 2 * kNS + kND, "block 0 P/dS late");
-  static_assert(2 * kNS + 2 + 7 / kPPS < 2 * kNS + 2 * kND && 2 * kNS + 2 + 15 / kPPS < 2 * kNS + 3 * kND,
-                "block 1 P/dS late");
+  constexpr int kKC = D / 16;          // 16-dim steps of S and dP per 32-row block
+  constexpr int kDB = D / 32;          // 32-dim blocks of dK^T / dV^T
+  constexpr int kHalf = 2 * kKC;       // products of S (dP) per tile = of dV (dK) = D / 8
+  constexpr int kPhase = 2 * kHalf;    // products per matrix phase
+  constexpr int kRing = 8;             // LDS operands in flight
+  static_assert(4 * kDB == kHalf, "dV / dK products per tile");
+  static_assert(kRing <= kHalf, "the ring reaches at most into the next phase's first half");
+  static_assert(kHalf % kRing == 0, "phases hold whole rings");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (kPairs - 1);
+  const bool s_wave = wave < kPairs;   // wave-uniform
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
   const int kb = blockIdx.x / p.BH;   // small key blocks (most work when causal) first
   const int bh = blockIdx.x % p.BH;
   const int k0 = kb * kBK;
-  const int key = k0 + wave * kKW + r32;
+  const int key = k0 + pair * kKW + r32;
 
   const unsigned head_q = (unsigned)p.Sq * G::kRowBytes;
   const unsigned head_k = (unsigned)p.Sk * G::kRowBytes;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + (size_t)bh * p.Sq * D, head_q);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + (size_t)bh * p.Sq * D, head_q);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (size_t)bh * p.Sk * D, head_k);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (size_t)bh * p.Sk * D, head_k);
-  // row terms: waves 0 and 2 load LSE*log2e, waves 1 and 3 load D
+  // the row term a dP wave loads: LSE log2(e) (pair 0) or D (pair 1)
   const __amdgpu_buffer_rsrc_t rrow =
-      make_rsrc(((wave & 1) ? p.dvec : p.lse2) + (size_t)bh * p.Sq, (unsigned)p.Sq * 4u);
+      make_rsrc((pair == 0 ? p.lse2 : p.dvec) + (size_t)bh * p.Sq, (unsigned)p.Sq * 4u);
 
   const int row_lane = row_lane_offset<D>(lane);
   const int tr_lane = tr_lane_offset<D>(lane);
-
-  // DS: the lane's dS values of a 16-row step (rows 8 (j / 4) + 4 g + j % 4,
-  // j < 8) are half g of its key's record in the step's position group of
-  // the tile's 128-row query block: one 16-byte buffer store whose per-tile
-  // part is a scalar offset
-  const size_t ds_slab = (size_t)p.ds_rows * kDsPositions;
-  const __amdgpu_buffer_rsrc_t rds =
-      make_rsrc(DS ? p.ds + (size_t)bh * p.ds_nqb * ds_slab : nullptr, DS ? (unsigned)(p.ds_nqb * ds_slab * 2) : 0u);
-  const int ds_lane = (key % kDsTileKeys) * kDsRecord + 16 * g;
-  const int ds_tile = (k0 + wave * kKW) / kDsTileKeys;   // wave-uniform
-
-  // B operands: the lane's K and V rows, dims 16 kc + 8 g .. +8
-  bf16x8 kf[kKC], vf[kKC];
-#pragma unroll
-  for (int kc = 0; kc < kKC; ++kc) {
-    const unsigned off = (unsigned)key * G::kRowBytes + (kc * 16 + 8 * g) * 2;
-    kf[kc] = __builtin_bit_cast(bf16x8, load16(rk, off));
-    vf[kc] = __builtin_bit_cast(bf16x8, load16(rv, off));
-    // only ever MFMA operands: keep them in the AGPR file (the s_nop covers
-    // the wait states between the moves and a first product right after)
-    asm volatile("s_nop 1" : "+a"(kf[kc]), "+a"(vf[kc]));
-  }
-
-  f32x16 dk[kDB], dv[kDB];
-#pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-    // the zeros are VALU writes: fix them here, two wait states ahead of the
-    // first product (otherwise they sink next to it)
-    asm volatile("s_nop 1" : "+a"(dk[db]), "+a"(dv[db]));
-  }
+  char* const pbuf = smem + L::kPOff + pair * L::kPPairBytes + lane * 16;   // + (4 b + i4) 1024
 
   // Tiles qt_lo .. n_qt-1.  qt_lo < n_qt always holds: causal requires
   // Sq == Sk and k0 < Sk, so k0 / kBQ <= (Sq - 1) / kBQ.
@@ -524,210 +511,347 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
   const int qt_lo = CAUSAL ? k0 / kBQ : 0;
   const int n = n_qt - qt_lo;
 
-  // relative tile t lives in stage t % kStages; the stage is always a
-  // compile-time constant below, so every LDS address is a loop-invariant
-  // lane offset plus an immediate
-  // memory-to-LDS loads of relative tile t into stage S: kPer per wave
-  auto issue = [&](int t, auto stage_tag) __attribute__((always_inline)) {
-    char* st = smem + decltype(stage_tag)::value * L::kStageBytes;
-    const int q0 = (qt_lo + t) * kBQ;
-    TileDMA<D, kBQ, kWaves>::load(rq, q0, st, wave, lane);
-    TileDMA<D, kBQ, kWaves>::load(rdo, q0, st + L::kTileBytes, wave, lane);
-    lds_dma4(rrow, (unsigned)(q0 + lane) * 4, st + L::kRowsOff + wave * kBQ * 4);
+  // the Q tile, the dO tile and the row terms (LSE log2(e), then D) of stage s
+  auto qtile = [&](int s) __attribute__((always_inline)) -> char* { return smem + L::kQOff + s * L::kTileBytes; };
+  auto otile = [&](int s) __attribute__((always_inline)) -> char* { return smem + L::kDoOff + s * L::kTileBytes; };
+  auto rows = [&](int s) __attribute__((always_inline)) -> float* {
+    return reinterpret_cast<float*>(smem + L::kRowsOff + s * L::kRowsBytes);
   };
-  // load i (0 <= i < kPer) of relative tile t into stage S, issued one at a
-  // time so that the loads of a tile spread over several MFMA steps
-  auto issue_one = [&](int t, auto stage_tag, auto load_tag) __attribute__((always_inline)) {
-    constexpr int i = decltype(load_tag)::value;
-    constexpr int kL = TileDMA<D, kBQ, kWaves>::kLoads;
-    char* st = smem + decltype(stage_tag)::value * L::kStageBytes;
+  // the loads of relative tile t into stage S, issued by the dP waves only:
+  // each its share of the Q and dO tiles, pairs 0 and 1 a row term
+  auto issue = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int st = decltype(stage_tag)::value;
     const int q0 = (qt_lo + t) * kBQ;
-    if constexpr (i < kL) {
-      TileDMA<D, kBQ, kWaves>::load_one(rq, q0, st, wave, lane, i);
-    } else if constexpr (i < 2 * kL) {
-      TileDMA<D, kBQ, kWaves>::load_one(rdo, q0, st + L::kTileBytes, wave, lane, i - kL);
-    } else {
-      lds_dma4(rrow, (unsigned)(q0 + lane) * 4, st + L::kRowsOff + wave * kBQ * 4);
-    }
+    TileDMA<D, kBQ, kPairs>::load(rq, q0, qtile(st), pair, lane);
+    TileDMA<D, kBQ, kPairs>::load(rdo, q0, otile(st), pair, lane);
+    if (pair < 2) lds_dma4(rrow, (unsigned)(q0 + lane) * 4, rows(st) + pair * kBQ);
   };
 
-  // operand j of a tile (j < 2 kNS: row reads of Q / dO for S / dP; then
-  // transposed reads of dO / Q for dV / dK)
-  auto op = [&](const char* st, int j) __attribute__((always_inline)) -> bf16x8 {
-    const char* qtile = st;
-    const char* otile = st + L::kTileBytes;
-    if (j < 2 * kNS) {
-      const int b = j / kNS, jj = j % kNS;
-      return (jj & 1) ? read_rows<D>(otile, row_lane, b, jj >> 1) : read_rows<D>(qtile, row_lane, b, jj >> 1);
-    }
-    const int jj = j - 2 * kNS;
-    const int ks = jj / kND, db = (jj >> 1) % kDB;
-    return (jj & 1) ? read_cols<D>(qtile, tr_lane, ks, db) : read_cols<D>(otile, tr_lane, ks, db);
-  };
+  // B operands: the lane's K row (S wave) or V row (dP wave), dims
+  // 16 kc + 8 g .. +8, loaded ahead of the tiles
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc((s_wave ? p.k : p.v) + (size_t)bh * p.Sk * D, head_k);
+  bf16x8 kvf[kKC];
+#pragma unroll
+  for (int kc = 0; kc < kKC; ++kc)
+    kvf[kc] = __builtin_bit_cast(bf16x8, load16(rkv, (unsigned)key * G::kRowBytes + (kc * 16 + 8 * g) * 2));
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   static_assert(kStages == 3, "stage constants below assume three stages");
+  static_assert(kBK / kBQ == 2, "two masked tiles per causal key block");
 
-  // ---- prologue: tiles 0, 1, 2 in flight; wait for tile 0
-  issue(0, S0{});
-  if (n > 1) issue(1, S1{});
-  if (n > 2) issue(2, S2{});
-  if (n > 2) wait_vmcnt<2 * kPer>();
-  else if (n > 1) wait_vmcnt<kPer>();
-  else wait_vmcnt<0>();
+  // ---- prologue: tiles 0 and 1 in flight; wait for tile 0
+  if (!s_wave) {
+    issue(0, S0{});
+    if (n > 1) {
+      issue(1, S1{});
+      if (pair < 2) wait_vmcnt<L::kTileLoads + 1>();
+      else wait_vmcnt<L::kTileLoads>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
   lds_barrier();
-  bf16x8 ring[kRing];
+
+  // phase barriers.  After A: the dP wave has used P(k) (its uses come
+  // before), so the S wave may overwrite it.  After B: P(k + 1) written
+  // (the S wave waits for its LDS writes), tile k + 2 landed (the dP waves
+  // wait for their loads; nothing later is in flight), tile k read by both.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto barrier_tiles = [&](auto lds_writes) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(lds_writes)::value) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // The matrix phases: the prelude's kHalf products (S(0) or dP(0)), then
+  // full phases of kHalf products of dV / dK for tile k and kHalf of S / dP
+  // for tile k + 1.  The ring holds the operands of the next products; past
+  // the phase's end they are the first products of the next phase (dV / dK
+  // of the following tile, always published by then).
+  using RS = RowStore<D>;
+  static_assert(kWaves * RS::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+
+  if (s_wave) {
+    // ================================================= S wave: S, P, dV
+    const bf16x8* kf = kvf;
+    f32x16 dv[kDB];
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) ring[j] = op(smem, j);
+    for (int db = 0; db < kDB; ++db) {
+      dv[db] = f32x16{};
+      asm volatile("s_nop 1" : "+v"(dv[db]));
+    }
+    // the products of a tile (row reads of Q for S; dO transposed for dV).
+    // Each kind's base is folded into the lane offset (it shares no bit
+    // with the lane offsets or the constants they are XORed with), hidden
+    // from the compiler so that a read is one lane register plus the
+    // stage's immediate offset.
+    int rl = row_lane + L::kQOff, tl = tr_lane + L::kDoOff;
+    asm volatile("" : "+v"(rl), "+v"(tl));
+    auto op_s = [&](int st, int j) __attribute__((always_inline)) -> bf16x8 {
+      return read_rows<D>(smem + st * L::kTileBytes, rl, j / kKC, j % kKC);
+    };
+    auto op_v = [&](int st, int j) __attribute__((always_inline)) -> bf16x8 {
+      return read_cols<D>(smem + st * L::kTileBytes, tl, j / kDB, j % kDB);
+    };
+    bf16x8 ring[kRing];
+    f32x16 s[2];
+    bf16x8 bp[4];
+    f32x4 lse[8];   // LSE log2(e) of the next P's rows, read ahead
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) ring[j] = op_s(0, j);
 
-  // One tile; MASK: apply the causal mask (only the first kBK / kBQ tiles of
-  // a causal key block hold keys after some of their rows).
-  // A tile's kPer loads: the first kRing (or all) in the steps after the
-  // barrier of the tile three before it, the rest in the first steps of the
-  // tile two before it (FIRST: tile 0, whose "tile two ahead" was loaded by
-  // the prologue).
-  constexpr int kEarly = kPer < kRing ? kPer : kRing;
-  auto tile = [&](int t, auto first_tag, auto mask_tag, auto stage_tag) __attribute__((always_inline)) {
-    constexpr bool FIRST = decltype(first_tag)::value;
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int kS = decltype(stage_tag)::value;   // == t % kStages
-    const char* cur = smem + kS * L::kStageBytes;
-    const char* nxt = smem + ((kS + 1) % kStages) * L::kStageBytes;
-    const int q0 = (qt_lo + t) * kBQ;
-    const float* lrow = reinterpret_cast<const float*>(cur + L::kRowsOff);   // LSE*log2e
-    const float* drow = lrow + kBQ;                                           // D
-    f32x16 s[2], dp[2];
-    bf16x8 bp[4], bs[4];      // bf16 P and dS of the four 16-row steps
-    float pe[16], de[16];     // P and dS of the block in progress
-    f32x4 l4[4], d4[4];       // LSE*log2e and D of its 16 rows
-    // causal: element i of block b is masked iff key - q0 - 32 b - 4 g > 8 (i / 4) + i % 4
-    const int delta0 = key - q0 - 4 * g;
-
-    static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
-      constexpr int j = J;
-      if constexpr (j == kBar) {
-        // every operand of tile t has been read; publish tile t + 1 (its
-        // loads were all issued before tile t; the kPer loads of tile t + 2
-        // may still run)
-        if (t + 2 < n) wait_vmcnt<kPer>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (j >= kBar && j - kBar < kEarly) {
-        if (t + 3 < n) issue_one(t + 3, stage_tag, std::integral_constant<int, j - kBar>{});
-      }
-      if constexpr (!FIRST && j < kPer - kEarly) {
-        if (t + 2 < n)
-          issue_one(t + 2, std::integral_constant<int, (decltype(stage_tag)::value + 2) % kStages>{},
-                    std::integral_constant<int, kEarly + j>{});
-      }
-      // DS: the four bf16 dS steps of this tile, after the barrier (so a
-      // whole tile passes before the next vmcnt wait, which counts them too)
-      // and before the next tile repacks them.  Non-temporal stores: dS is
-      // read once, by the other kernel, and left in the L2 it would evict
-      // the Q / dO tiles every key block of the head re-reads (measured:
-      // +35 MiB of refetches per launch with ordinary stores)
-      if constexpr (DS && j >= kSteps - 4) {
-        constexpr int x = j - (kSteps - 4);
-        constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
-        const int pg = (q0 % kDsPositions) / kDsGroup + x;
-        const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) +
-                         (ds_tile * (kDsPositions / kDsGroup) + pg) * (kDsTileBytes / (kDsPositions / kDsGroup));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
-      }
-      const bf16x8 a = ring[j % kRing];
-      if constexpr (j + kRing < kSteps) ring[j % kRing] = op(cur, j + kRing);
-      else ring[j % kRing] = op(nxt, j + kRing - kSteps);
-      // S, dP accumulate in VGPRs (read by the P / dS arithmetic), dK, dV in
-      // AGPRs (read once, at the end); K and V are AGPR operands
-      if constexpr (j < 2 * kNS) {
-        constexpr int b = j / kNS, jj = j % kNS;
-        if constexpr (jj < 2) {
-          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::init_v(dp[b], a, vf[jj >> 1]);
-          else MfmaAsm<'v', 'a'>::init_v(s[b], a, kf[jj >> 1]);
-        } else {
-          if constexpr (jj & 1) MfmaAsm<'v', 'a'>::acc_v(dp[b], a, vf[jj >> 1]);
-          else MfmaAsm<'v', 'a'>::acc_v(s[b], a, kf[jj >> 1]);
+    // a matrix phase: NV (0 or kHalf) products of dV for the tile in stage
+    // CUR, then kHalf of S for the tile in stage NXT; operands past the end
+    // are the next phase's first dV operands (tile in NXT).  Near its end
+    // the rows' LSE of the tile in NXT is read for the P that follows.
+    auto mphase = [&](auto nv_tag, auto cur_tag, auto nxt_tag) __attribute__((always_inline)) {
+      constexpr int NV = decltype(nv_tag)::value;
+      constexpr int kN = NV + kHalf;
+      constexpr int cur = decltype(cur_tag)::value;
+      constexpr int nxt = decltype(nxt_tag)::value;
+      // operand o of this phase
+      auto op = [&](int o) __attribute__((always_inline)) -> bf16x8 {
+        return o < NV ? op_v(cur, o) : op_s(nxt, o - NV);
+      };
+      static_for<kN>([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = J;
+        if constexpr (j == kN - kRing) {
+          static_for<8>([&](auto X) __attribute__((always_inline)) {
+            constexpr int x = X;   // elements 4 (x % 4) .. +3 of block x / 4
+            lse[x] = *reinterpret_cast<const f32x4*>(rows(nxt) + 32 * (x / 4) + 8 * (x % 4) + 4 * g);
+          });
         }
-      } else {
-        constexpr int jj = j - 2 * kNS;
-        constexpr int ks = jj / kND, db = (jj >> 1) % kDB;
-        if constexpr (jj & 1) MfmaAsm<'v', 'v'>::acc_a(dk[db], a, bs[ks]);
-        else MfmaAsm<'v', 'v'>::acc_a(dv[db], a, bp[ks]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // P / dS of block b, elements from step (b + 1) kNS + 2 on
+        const bf16x8 a = ring[j % kRing];
+        constexpr int jn = j + kRing;
+        if constexpr (jn < kN) ring[j % kRing] = op(jn);
+        else if constexpr (jn - kN < kRing) ring[j % kRing] = op_v(nxt, jn - kN);
+        if constexpr (j < NV) {
+          MfmaAsm<'v', 'v'>::acc_v(dv[j % kDB], a, bp[j / kDB]);
+        } else {
+          constexpr int b = (j - NV) / kKC, kc = (j - NV) % kKC;
+          if constexpr (kc == 0) MfmaAsm<'v', 'v'>::init_v(s[b], a, kf[0]);
+          else MfmaAsm<'v', 'v'>::acc_v(s[b], a, kf[kc]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // P of relative tile t: float32 to LDS, bf16 into bp
+    auto vphase = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // causal: element i of block b is masked iff key - q0 - 32 b - 4 g > 8 (i / 4) + i % 4
+      const int delta0 = key - (qt_lo + t) * kBQ - 4 * g;
+      mfma_drain_v2(s[0], s[1]);
       static_for<2>([&](auto B) __attribute__((always_inline)) {
         constexpr int b = B;
-        constexpr int first = (b + 1) * kNS + 2;
-        // row terms of elements 4 i4 .. 4 i4 + 3, three steps before their use
+        float pe[16];
         static_for<4>([&](auto I4) __attribute__((always_inline)) {
           constexpr int i4 = I4;
-          if constexpr (j == first + (4 * i4) / kPPS - 3) {
-            l4[i4] = *reinterpret_cast<const f32x4*>(lrow + 32 * b + 8 * i4 + 4 * g);
-            d4[i4] = *reinterpret_cast<const f32x4*>(drow + 32 * b + 8 * i4 + 4 * g);
-          }
+          const f32x4 l4 = lse[4 * b + i4];
+          static_for<4>([&](auto U) __attribute__((always_inline)) {
+            constexpr int u = U, i = 4 * i4 + u;
+            float x = __builtin_fmaf(s[b][i], p.scale_log2, -l4[u]);
+            if (MASK && delta0 - 32 * b > 8 * i4 + u) x = kNegInf;
+            pe[i] = exp2_hw(x);
+          });
+          *reinterpret_cast<f32x4*>(pbuf + (4 * b + i4) * 1024) =
+              f32x4{pe[4 * i4], pe[4 * i4 + 1], pe[4 * i4 + 2], pe[4 * i4 + 3]};
         });
-        // the last S / dP products of block b were issued two and three steps ago
-        if constexpr (j == first) mfma_drain_v2(s[b], dp[b]);
-        static_for<kPPS>([&](auto U) __attribute__((always_inline)) {
-          constexpr int i = (j - first) * kPPS + U;
-          if constexpr (i >= 0 && i < 16) {
-            float x = __builtin_fmaf(s[b][i], p.scale_log2, -l4[i >> 2][i & 3]);
-            if (MASK && delta0 - 32 * b > 8 * (i >> 2) + (i & 3)) x = kNegInf;
-            const float pv = exp2_hw(x);
-            pe[i] = pv;
-            de[i] = pv * (dp[b][i] - d4[i >> 2][i & 3]);
-            if constexpr ((i & 7) == 7) {
-              constexpr int h = i - 7;
-              bp[2 * b + (i >> 3)] = pack_bf16x8(pe[h], pe[h + 1], pe[h + 2], pe[h + 3], pe[h + 4], pe[h + 5],
-                                                 pe[h + 6], pe[h + 7]);
-              bs[2 * b + (i >> 3)] = pack_bf16x8(de[h], de[h + 1], de[h + 2], de[h + 3], de[h + 4], de[h + 5],
-                                                 de[h + 6], de[h + 7]);
-              // keep this work at this step (the IR optimiser would sink it
-              // next to the products that use it)
-              asm volatile("" ::"v"(bp[2 * b + (i >> 3)]), "v"(bs[2 * b + (i >> 3)]));
-            }
-          }
-        });
+        bp[2 * b] = pack_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+        bp[2 * b + 1] = pack_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
       });
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  // tiles 0 and 1 (stages 0, 1; masked if causal), then the rest from stage
-  // 2 on, three tiles per loop pass
-  static_assert(kBK / kBQ == 2, "two masked tiles per causal key block");
-  using M = std::integral_constant<bool, CAUSAL>;
-  using F = std::false_type;
-  using T = std::true_type;
-  tile(0, T{}, M{}, S0{});
-  if (n > 1) tile(1, F{}, M{}, S1{});
-  int t = 2;
-  while (t < n) {
-    tile(t, F{}, F{}, S2{});
-    if (++t >= n) break;
-    tile(t, F{}, F{}, S0{});
-    if (++t >= n) break;
-    tile(t, F{}, F{}, S1{});
-    ++t;
-  }
+      // two wait states before a product reads them
+      asm volatile("s_nop 1" ::"v"(bp[0]), "v"(bp[1]), "v"(bp[2]), "v"(bp[3]));
+    };
+    using Z = std::integral_constant<int, 0>;
+    using H = std::integral_constant<int, kHalf>;
+    // prelude: S(0) | P(0)
+    mphase(Z{}, S0{}, S0{});
+    barrier();
+    vphase(0, std::integral_constant<bool, CAUSAL>{});
+    barrier_tiles(std::true_type{});
+    // interval k: A(k) = dV(k), S(k + 1) | B(k) = P(k + 1)
+    auto interval = [&](int k, auto mask_tag, auto st_tag) __attribute__((always_inline)) {
+      constexpr int c = decltype(st_tag)::value;
+      using C1 = std::integral_constant<int, (c + 1) % kStages>;
+      mphase(H{}, st_tag, C1{});
+      barrier();
+      vphase(k + 1, mask_tag);
+      barrier_tiles(std::true_type{});
+    };
+    // P(1) is the last masked tile when causal
+    interval(0, std::integral_constant<bool, CAUSAL>{}, S0{});
+    int k = 1;
+    while (k < n) {
+      interval(k, std::false_type{}, S1{});
+      if (++k >= n) break;
+      interval(k, std::false_type{}, S2{});
+      if (++k >= n) break;
+      interval(k, std::false_type{}, S0{});
+      ++k;
+    }
 
-  // ---- dK = scale (dK^T)^T, dV = (dV^T)^T -> bf16 (lane = key)
+    // ---- dV = (dV^T)^T -> bf16 (lane = key), whole-row stores through LDS
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    mfma_drain_a(dk[db]);
-    mfma_drain_a(dv[db]);
+    for (int db = 0; db < kDB; ++db) mfma_drain_v(dv[db]);
+    dma_barrier();
+    RS::store(smem + wave * RS::kBytes, dv, 1.0f, p.dv + (size_t)bh * p.Sk * D, k0 + pair * kKW, p.Sk, lane);
+  } else {
+    // ================================================ dP wave: dP, dS, dK
+    const bf16x8* vf = kvf;
+    f32x16 dk[kDB];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      dk[db] = f32x16{};
+      asm volatile("s_nop 1" : "+v"(dk[db]));
+    }
+    // DS: the lane's dS values of a 16-row step (rows 8 (j / 4) + 4 g + j % 4,
+    // j < 8) are half g of its key's record in the step's position group of
+    // the tile's 128-row query block: one 16-byte buffer store whose per-tile
+    // part is a scalar offset
+    const size_t ds_slab = (size_t)p.ds_rows * kDsPositions;
+    const __amdgpu_buffer_rsrc_t rds = make_rsrc(DS ? p.ds + (size_t)bh * p.ds_nqb * ds_slab : nullptr,
+                                                 DS ? (unsigned)(p.ds_nqb * ds_slab * 2) : 0u);
+    const int ds_lane = (key % kDsTileKeys) * kDsRecord + 16 * g;
+    const int ds_tile = (k0 + pair * kKW) / kDsTileKeys;   // wave-uniform
+
+    // the products of a tile (row reads of dO for dP; Q transposed for dK),
+    // the kinds' bases folded into the lane offsets as in the S wave
+    int rl = row_lane + L::kDoOff, tl = tr_lane + L::kQOff;
+    asm volatile("" : "+v"(rl), "+v"(tl));
+    auto op_p = [&](int st, int j) __attribute__((always_inline)) -> bf16x8 {
+      return read_rows<D>(smem + st * L::kTileBytes, rl, j / kKC, j % kKC);
+    };
+    auto op_k = [&](int st, int j) __attribute__((always_inline)) -> bf16x8 {
+      return read_cols<D>(smem + st * L::kTileBytes, tl, j / kDB, j % kDB);
+    };
+    bf16x8 ring[kRing];
+    f32x16 dp[2];
+    bf16x8 bs[4];
+    f32x4 dr[8];   // D of the next dS's rows, read ahead
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) ring[j] = op_p(0, j);
+
+    // a matrix phase: NK (0 or kHalf) products of dK for the tile in CUR,
+    // then kHalf of dP for the tile in NXT; operands past the end are the
+    // next phase's first dK operands (tile in NXT).  Near its end the rows'
+    // D of the tile in NXT is read for the dS that follows.
+    auto mphase = [&](auto nk_tag, auto cur_tag, auto nxt_tag) __attribute__((always_inline)) {
+      constexpr int NK = decltype(nk_tag)::value;
+      constexpr int kN = NK + kHalf;
+      constexpr int cur = decltype(cur_tag)::value;
+      constexpr int nxt = decltype(nxt_tag)::value;
+      auto op = [&](int o) __attribute__((always_inline)) -> bf16x8 {
+        return o < NK ? op_k(cur, o) : op_p(nxt, o - NK);
+      };
+      static_for<kN>([&](auto J) __attribute__((always_inline)) {
+        constexpr int j = J;
+        if constexpr (j == kN - kRing) {
+          static_for<8>([&](auto X) __attribute__((always_inline)) {
+            constexpr int x = X;
+            dr[x] = *reinterpret_cast<const f32x4*>(rows(nxt) + kBQ + 32 * (x / 4) + 8 * (x % 4) + 4 * g);
+          });
+        }
+        const bf16x8 a = ring[j % kRing];
+        constexpr int jn = j + kRing;
+        if constexpr (jn < kN) ring[j % kRing] = op(jn);
+        else if constexpr (jn - kN < kRing) ring[j % kRing] = op_k(nxt, jn - kN);
+        if constexpr (j < NK) {
+          MfmaAsm<'v', 'v'>::acc_v(dk[j % kDB], a, bs[j / kDB]);
+        } else {
+          constexpr int b = (j - NK) / kKC, kc = (j - NK) % kKC;
+          if constexpr (kc == 0) MfmaAsm<'v', 'v'>::init_v(dp[b], a, vf[0]);
+          else MfmaAsm<'v', 'v'>::acc_v(dp[b], a, vf[kc]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // dS of tile k from P in LDS and dP: bf16 into bs (and, DS, to the dS^T
+    // buffer).  P is read first, in two batches, then the loads of tile
+    // k + 2 are issued (memory-to-LDS loads hold up the issuing wave for a
+    // while, here overlapping the P reads)
+    auto vphase = [&](int k, auto load_stage) __attribute__((always_inline)) {
+      f32x4 pl[8];
+      static_for<4>([&](auto X) __attribute__((always_inline)) {
+        pl[X] = *reinterpret_cast<const f32x4*>(pbuf + X * 1024);
+      });
+      if (k + 2 < n) issue(k + 2, load_stage);
+      mfma_drain_v2(dp[0], dp[1]);
+      static_for<2>([&](auto B) __attribute__((always_inline)) {
+        constexpr int b = B;
+        if constexpr (b == 0) {
+          static_for<4>([&](auto X) __attribute__((always_inline)) {
+            pl[4 + X] = *reinterpret_cast<const f32x4*>(pbuf + (4 + X) * 1024);
+          });
+        }
+        float de[16];
+        static_for<4>([&](auto I4) __attribute__((always_inline)) {
+          constexpr int i4 = I4;
+          const f32x4 pv = pl[4 * b + i4];
+          const f32x4 d4 = dr[4 * b + i4];
+          static_for<4>([&](auto U) __attribute__((always_inline)) {
+            constexpr int u = U, i = 4 * i4 + u;
+            de[i] = pv[u] * (dp[b][i] - d4[u]);
+          });
+        });
+        bs[2 * b] = pack_bf16x8(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
+        bs[2 * b + 1] = pack_bf16x8(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+      });
+      asm volatile("s_nop 1" ::"v"(bs[0]), "v"(bs[1]), "v"(bs[2]), "v"(bs[3]));
+      if constexpr (DS) {
+        // Non-temporal stores: dS is read once, by the other kernel, and
+        // left in the L2 it would evict the Q / dO tiles every key block of
+        // the head re-reads
+        const int q0 = (qt_lo + k) * kBQ;
+        constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
+        static_for<4>([&](auto X) __attribute__((always_inline)) {
+          constexpr int x = X;
+          const int pg = (q0 % kDsPositions) / kDsGroup + x;
+          const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) +
+                           (ds_tile * (kDsPositions / kDsGroup) + pg) * (kDsTileBytes / (kDsPositions / kDsGroup));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
+        });
+      }
+    };
+    using Z = std::integral_constant<int, 0>;
+    using H = std::integral_constant<int, kHalf>;
+    // prelude: (idle) | dP(0)
+    barrier();
+    mphase(Z{}, S0{}, S0{});
+    barrier_tiles(std::false_type{});
+    // interval k: A(k) = dS(k) | B(k) = dK(k), dP(k + 1)
+    auto interval = [&](int k, auto st_tag) __attribute__((always_inline)) {
+      constexpr int c = decltype(st_tag)::value;
+      using C1 = std::integral_constant<int, (c + 1) % kStages>;
+      using C2 = std::integral_constant<int, (c + 2) % kStages>;
+      vphase(k, C2{});
+      barrier();
+      mphase(H{}, st_tag, C1{});
+      barrier_tiles(std::false_type{});
+    };
+    interval(0, S0{});
+    int k = 1;
+    while (k < n) {
+      interval(k, S1{});
+      if (++k >= n) break;
+      interval(k, S2{});
+      if (++k >= n) break;
+      interval(k, S0{});
+      ++k;
+    }
+
+    // ---- dK = scale (dK^T)^T -> bf16 (lane = key), whole-row stores through LDS
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) mfma_drain_v(dk[db]);
+    dma_barrier();
+    RS::store(smem + wave * RS::kBytes, dk, p.scale, p.dk + (size_t)bh * p.Sk * D, k0 + pair * kKW, p.Sk, lane);
   }
-  // whole-row stores through LDS, once every wave has read its last tile
-  using RS = RowStore<D>;
-  static_assert(2 * kWaves * RS::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
-  dma_barrier();
-  RS::store(smem + wave * RS::kBytes, dk, p.scale, p.dk + (size_t)bh * p.Sk * D, k0 + wave * kKW, p.Sk, lane);
-  RS::store(smem + (kWaves + wave) * RS::kBytes, dv, 1.0f, p.dv + (size_t)bh * p.Sk * D, k0 + wave * kKW, p.Sk,
-            lane);
 }
 
 // ============================================================ dQ from dS
