@@ -662,6 +662,10 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
           });
           *reinterpret_cast<f32x4*>(pbuf + (4 * b + i4) * 1024) =
               f32x4{pe[4 * i4], pe[4 * i4 + 1], pe[4 * i4 + 2], pe[4 * i4 + 3]};
+          // each write in place, between its elements' arithmetic: the
+          // compiler would gather them into bursts, which stall the other
+          // wave's operand reads (measured: ~250 cycles more per tile)
+          __builtin_amdgcn_sched_barrier(0);
         });
         bp[2 * b] = pack_bf16x8(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
         bp[2 * b + 1] = pack_bf16x8(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
@@ -802,22 +806,23 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
         });
         bs[2 * b] = pack_bf16x8(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
         bs[2 * b + 1] = pack_bf16x8(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+        if constexpr (DS) {
+          // each block's two dS steps stored as soon as they are packed.
+          // Non-temporal stores: dS is read once, by the other kernel, and
+          // left in the L2 it would evict the Q / dO tiles every key block
+          // of the head re-reads
+          const int q0 = (qt_lo + k) * kBQ;
+          constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
+          static_for<2>([&](auto X) __attribute__((always_inline)) {
+            constexpr int x = 2 * b + X;
+            const int pg = (q0 % kDsPositions) / kDsGroup + x;
+            const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) +
+                             (ds_tile * (kDsPositions / kDsGroup) + pg) * (kDsTileBytes / (kDsPositions / kDsGroup));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
+          });
+        }
       });
       asm volatile("s_nop 1" ::"v"(bs[0]), "v"(bs[1]), "v"(bs[2]), "v"(bs[3]));
-      if constexpr (DS) {
-        // Non-temporal stores: dS is read once, by the other kernel, and
-        // left in the L2 it would evict the Q / dO tiles every key block of
-        // the head re-reads
-        const int q0 = (qt_lo + k) * kBQ;
-        constexpr int kNonTemporal = 2;   // cache-policy bit of the buffer store
-        static_for<4>([&](auto X) __attribute__((always_inline)) {
-          constexpr int x = X;
-          const int pg = (q0 % kDsPositions) / kDsGroup + x;
-          const int soff = (q0 / kDsPositions) * p.ds_rows * (kDsPositions * 2) +
-                           (ds_tile * (kDsPositions / kDsGroup) + pg) * (kDsTileBytes / (kDsPositions / kDsGroup));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bs[x]), rds, ds_lane, soff, kNonTemporal);
-        });
-      }
     };
     using Z = std::integral_constant<int, 0>;
     using H = std::integral_constant<int, kHalf>;
