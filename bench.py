@@ -336,8 +336,8 @@ def main():
         parts += [("bwd_dq_kernel", lambda: bwd_phase(fa.FA_BWD_PREPARE | fa.FA_BWD_DQ)),
                   ("bwd_dkdv_kernel", lambda: bwd_phase(fa.FA_BWD_DKDV))]
 
-    # ---- clock warm-up and W warmup steps, then exactly K timed steps with
-    # events between kernels
+    # ---- clock warm-up and W warmup steps, then exactly K timed steps, then
+    # K steps with events between the kernels
     def step():
         for _, fn in parts:
             fn()
@@ -349,19 +349,32 @@ def main():
         for _, fn in parts:
             fn()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    # the K timed steps: one event before the first and one after the last
+    # (events between the kernels are not part of the step: they add ~10 us
+    # per step of queue work)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     t_wall0 = time.perf_counter()
+    e_start.record()
+    for _ in range(args.steps):
+        for _, fn in parts:
+            fn()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    step_ms = e_start.elapsed_time(e_end) / args.steps
+    # then K more steps with an event between every two kernels, on the
+    # stream they run on, for each kernel's average duration
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     for e in evs:
         e[0].record()
         for i, (_, fn) in enumerate(parts):
             fn()
             e[i + 1].record()
     torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall0
     sclk.__exit__(None, None, None)
     part_all = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(len(parts))]
     part_ms = [sum(x) / args.steps for x in part_all]
-    step_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
 
     # counted FLOPs (the configs' convention) and each kernel's own algorithmic
     # work per (query, key) pair: forward 4d; dQ kernel 6d (S, dP, dQ; its row
