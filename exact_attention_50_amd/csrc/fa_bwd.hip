@@ -863,9 +863,12 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 // Five-product form: dQ = scale dS K from the dS^T buffer (layout above) and
 // K.  A workgroup owns one slab (128 query rows) and streams 64-key tiles of
 // K and of the slab, memory-to-LDS, through a ring of kStages stages issued
-// kStages - 1 tiles ahead; per tile and wave (positions 32 w .. +32):
-//   dQ^T (D x 32) += K^T (D x 64 keys) . dS^T (64 keys x 32),
+// kStages - 1 tiles ahead.  Eight waves, two per SIMD: wave w takes positions
+// 32 (w % 4) .. +32 and the half h = w / 4 of the D dims; per tile
+//   dQ^T (D/2 x 32) += K^T (dims of half h x 64 keys) . dS^T (64 keys x 32),
 // both operands read transposed, so their k slots (keys) follow one order.
+// (Two waves per SIMD: one issues its transposed LDS reads while the other
+// waits on its own.)
 // The K tile has the layout of fa_tiles.hpp.  The dS tile is the slab's 8
 // groups x 64 records (2 KB per group); in odd groups record r holds key
 // r ^ 4, so the two 16-lane halves of a transposed read pass (groups 2 w and
@@ -879,8 +882,9 @@ __global__ __launch_bounds__(kvk::kThreads, 1) void bwd_dkdv_kernel(BwdParams p)
 // past the diagonal, and those are exactly the tiles the dK/dV kernel
 // wrote).  HBM-bound: dS is read once.
 namespace dsk {
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kPosBlocks = 4;   // 32-position blocks of a slab
 constexpr int kBN = 64;
 constexpr int kStages = 4;
 constexpr int kSlabTiles = kBN / kDsTileKeys;   // slab tiles per key tile
@@ -893,6 +897,7 @@ struct Layout {
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kKLoads = TileDMA<D, kBN, kWaves>::kLoads;
   static constexpr int kPer = kKLoads + kSLoads;
+  static constexpr int kOutPitch = D * 2 + 16;   // output staging: bf16 rows padded by 16 bytes
 };
 }  // namespace dsk
 
@@ -900,16 +905,17 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p) {
   using namespace dsk;
   using L = Layout<D>;
-  constexpr int kDB = D / 32;
+  constexpr int kDBW = D / 64;                // 32-dim blocks per wave (half of D)
   constexpr int kPer = L::kPer;
-  constexpr int kSteps = (kBN / 16) * kDB;   // products per tile and wave
-  constexpr int kAhead = 4;                  // K^T operands in flight
-  static_assert(kWaves * 32 == kDsPositions, "one 32-position block per wave");
+  constexpr int kSteps = (kBN / 16) * kDBW;   // products per tile and wave
+  constexpr int kAhead = 4;                   // K^T operands in flight
+  static_assert(kPosBlocks * 32 == kDsPositions && kWaves == 2 * kPosBlocks, "two waves per position block");
   static_assert(kPer <= kSteps, "one load per product at most");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pw = wave % kPosBlocks, dh = wave / kPosBlocks;
   const int qb = p.ds_nqb - 1 - (int)blockIdx.x / p.BH;   // most key tiles first when causal
   const int bh = (int)blockIdx.x % p.BH;
   const int n_all = (p.Sk + kBN - 1) / kBN;
@@ -919,7 +925,9 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
       make_rsrc(p.k + (size_t)bh * p.Sk * D, (unsigned)p.Sk * TileGeom<D>::kRowBytes);
   const size_t slab = (size_t)p.ds_rows * kDsPositions;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.ds + ((size_t)bh * p.ds_nqb + qb) * slab, (unsigned)(slab * 2));
-  const int tr_k = tr_lane_offset<D>(lane);
+  // dims 32 (kDBW dh + j) .. +32 of the K^T operand: the transposed-read lane
+  // offset XOR 64 (kDBW dh + j), the wave's part folded in once
+  const int tr_k = tr_lane_offset<D>(lane) ^ (64 * kDBW * dh);
   // dS load i of this wave: 1 KB of LDS, blk = i kWaves + w: slab tile
   // kSlabTiles t + blk / 16, records 32 c .. +32 of its group pg (blk % 16 =
   // 2 pg + c); lane l fetches half l % 2 of record 32 c + l / 2.  The LDS
@@ -939,10 +947,10 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     return (unsigned)(st * kDsTileBytes + (pg * kDsTileKeys + rec) * kDsRecord + 16 * (lane & 1));
   };
   // B operand (dS^T, k = keys of step ks in accumulator order, n = position
-  // 32 w + lane % 32): two ds_read_b64_tr_b16 over 4 records x 16 positions of
-  // group pg = 2 w + h, h = (lane / 16) % 2; rows 16 ks + 4 g + s / 4 (and + 8)
+  // 32 pw + lane % 32): two ds_read_b64_tr_b16 over 4 records x 16 positions of
+  // group pg = 2 pw + h, h = (lane / 16) % 2; rows 16 ks + 4 g + s / 4 (and + 8)
   const int s16 = lane & 15, hh = (lane >> 4) & 1, gg = lane >> 5;
-  const int tr_s = ((2 * wave + hh) * kDsTileKeys + 4 * (gg ^ hh) + (s16 >> 2)) * kDsRecord + 8 * (s16 & 3);
+  const int tr_s = ((2 * pw + hh) * kDsTileKeys + 4 * (gg ^ hh) + (s16 >> 2)) * kDsRecord + 8 * (s16 & 3);
   auto read_s = [&](const char* stile, int ks) __attribute__((always_inline)) -> bf16x8 {
     constexpr int kStepsPerSlabTile = kDsTileKeys / 16;
     const char* base = stile + (ks / kStepsPerSlabTile) * kDsTileBytes + tr_s;
@@ -961,9 +969,9 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     }
   };
 
-  f32x16 acc[kDB];
+  f32x16 acc[kDBW];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) acc[db] = f32x16{};
+  for (int j = 0; j < kDBW; ++j) acc[j] = f32x16{};
 
   constexpr int kLead = kStages - 1;   // tiles in flight ahead of the one in use
   static_for<kLead>([&](auto U) __attribute__((always_inline)) {
@@ -990,13 +998,14 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     bf16x8 a[kAhead];
     static_for<kBN / 16>([&](auto KS) __attribute__((always_inline)) { b[KS] = read_s(stile, KS); });
     static_for<kAhead>([&](auto J) __attribute__((always_inline)) {
-      a[J] = read_cols<D>(kt, tr_k, J / kDB, J % kDB);
+      a[J] = read_cols<D>(kt, tr_k, J / kDBW, J % kDBW);
     });
     static_for<kSteps>([&](auto J) __attribute__((always_inline)) {
       constexpr int j = J;
-      constexpr int ks = j / kDB, db = j % kDB;
+      constexpr int ks = j / kDBW, db = j % kDBW;
       const bf16x8 a_j = a[j % kAhead];
-      if constexpr (j + kAhead < kSteps) a[j % kAhead] = read_cols<D>(kt, tr_k, (j + kAhead) / kDB, (j + kAhead) % kDB);
+      if constexpr (j + kAhead < kSteps)
+        a[j % kAhead] = read_cols<D>(kt, tr_k, (j + kAhead) / kDBW, (j + kAhead) % kDBW);
       constexpr int every = kSteps / kPer;
       if constexpr (j % every == 0 && j / every < kPer) {
         if (more) load_one(t + kLead, j / every);
@@ -1006,12 +1015,39 @@ __global__ __launch_bounds__(dsk::kThreads, 1) void bwd_dq_ds_kernel(BwdParams p
     });
   }
 
-  // dQ = scale (dQ^T)^T -> bf16; lane r + 32 g holds position 32 w + r, i.e.
-  // query row 32 w + r with bits 2 and 3 exchanged
-  static_assert(kWaves * RowStore<D>::kBytes <= L::kLdsBytes, "output staging exceeds the LDS ring");
+  // dQ = scale (dQ^T)^T -> bf16.  In the MFMA C layout lane r + 32 g holds
+  // position 32 pw + r' (r' = r with bits 2 and 3 exchanged: the row order of
+  // the transposed dS^T reads) at dims 32 (kDBW dh + j) + 8 (i / 4) + 4 g + i % 4
+  // of acc[j][i]; the slab's 128 x D rows are staged in LDS (8-byte writes,
+  // rows padded so they meet every bank once per 16 rows), then stored 16
+  // bytes per lane over whole rows, rows past Sq skipped
+  static_assert(kDsPositions * L::kOutPitch <= L::kLdsBytes, "output staging exceeds the LDS ring");
   dma_barrier();
-  RowStore<D>::store(smem + wave * RowStore<D>::kBytes, acc, p.scale, p.dq + (size_t)bh * p.Sq * D,
-                     qb * kDsPositions + 32 * wave, p.Sq, lane, /*swap23=*/true);
+  {
+    const int r = lane & 31, g = lane >> 5;
+    char* srow = smem + (32 * pw + ((r & 19) | ((r & 4) << 1) | ((r & 8) >> 1))) * L::kOutPitch;
+#pragma unroll
+    for (int j = 0; j < kDBW; ++j)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 v = {acc[j][4 * i4 + 0] * p.scale, acc[j][4 * i4 + 1] * p.scale, acc[j][4 * i4 + 2] * p.scale,
+                         acc[j][4 * i4 + 3] * p.scale};
+        *reinterpret_cast<bf16x4*>(srow + (32 * (kDBW * dh + j) + 8 * i4 + 4 * g) * 2) =
+            __builtin_convertvector(v, bf16x4);
+      }
+  }
+  lds_barrier();
+  constexpr int kChunks = D / 8;   // 16-byte chunks per row
+  static_assert(kDsPositions * kChunks % kThreads == 0, "whole chunks per thread");
+  bf16* out = p.dq + (size_t)bh * p.Sq * D;
+#pragma unroll
+  for (int it = 0; it < kDsPositions * kChunks / kThreads; ++it) {
+    const int q = it * kThreads + (int)threadIdx.x;
+    const int row = q / kChunks, c = q % kChunks;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(smem + row * L::kOutPitch + c * 16);
+    const int qrow = qb * kDsPositions + row;
+    if (qrow < p.Sq) *reinterpret_cast<u32x4*>(out + (size_t)qrow * D + c * 8) = val;
+  }
 }
 
 template <typename K>
