@@ -123,18 +123,19 @@ def gradient_tile_cycles_cdna4(M_own, N_stream, d, products, row_reads, tr_reads
     return c
 
 
-def ds_product_tile_cycles_cdna4(M_own, N_stream, d, waves=4, hw=MI355X_CU):
+def ds_product_tile_cycles_cdna4(M_own, N_stream, d, waves=4, d_parts=1, hw=MI355X_CU):
     """CU cycles of each unit for one tile of the dQ = dS K kernel of the
     five-product form: a workgroup of ``waves`` wavefronts owning M_own query
-    rows (32 per wavefront) against N_stream keys.  mma = one product,
-    2 M N d FLOPs; lds = every wavefront reads the K tile transposed
-    (N d bf16) and its 32 columns of the dS tile transposed (N x 32 bf16),
-    at the transposed-read rate, halved below 8 wavefronts per CU (the reads
-    are latency bound there); hbm = the dS tile, M N bf16 values, streamed
-    from HBM once (K is re-read from L2); no exponentials, no VALU work to
-    speak of."""
+    rows against N_stream keys, each 32 rows taken by ``d_parts`` wavefronts
+    with d / d_parts of the dims each.  mma = one product, 2 M N d FLOPs;
+    lds = every wavefront reads its share of the K tile transposed
+    (N d / d_parts bf16) and its 32 columns of the dS tile transposed
+    (N x 32 bf16), at the transposed-read rate, halved below 8 wavefronts
+    per CU (the reads are latency bound there); hbm = the dS tile, M N bf16
+    values, streamed from HBM once (K is re-read from L2); no exponentials,
+    no VALU work to speak of."""
     mma = 2.0 * M_own * N_stream * d / hw["mma_flops_per_clk"]
-    tr_bytes = (M_own / 32) * (N_stream * d + N_stream * 32) * 2
+    tr_bytes = (M_own / 32) * d_parts * (N_stream * d / d_parts + N_stream * 32) * 2
     rate = hw["lds_tr_bytes_per_clk"] * (1.0 if waves >= 8 else 0.5)
     lds = tr_bytes / rate
     hbm = M_own * N_stream * 2 / hbm_bytes_per_clk(hw)

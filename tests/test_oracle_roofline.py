@@ -105,5 +105,10 @@ def test_cdna4_hbm_terms_hand_derived():
     assert name == "lds" and _close(frac["mma"], 0.4) and _close(frac["hbm"], 1258.2912 / 1280.0)
     c8 = roofline.ds_product_tile_cycles_cdna4(128, 64, 128, waves=8)
     assert _close(c8["lds"], 640.0) and roofline.bound(c8)[0] == "hbm"
+    # two wavefronts per 32 rows, half of the dims each: the K tile once per
+    # row block, the dS columns twice
+    c8h = roofline.ds_product_tile_cycles_cdna4(128, 64, 128, waves=8, d_parts=2)
+    assert _close(c8h["lds"], 4 * (64 * 128 + 2 * 64 * 32) * 2 / 128.0) and _close(c8h["lds"], 768.0)
+    assert _close(c8h["mma"], 512.0) and roofline.bound(c8h)[0] == "hbm"
     c64 = roofline.ds_product_tile_cycles_cdna4(128, 64, 64)
     assert _close(c64["mma"], 256.0) and _close(c64["lds"], 4 * (64 * 64 + 64 * 32) * 2 / 64.0)
