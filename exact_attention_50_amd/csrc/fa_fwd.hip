@@ -70,6 +70,7 @@ struct FwdParams {
   int k_len;
   int q_off;         // global index of query row 0 (causal: key j visible iff k_begin + j <= q_off + i)
   int n_qblocks;
+  int paired;        // causal, n_qblocks even: workgroup (r, bh) runs ranks r and n_qblocks - 1 - r
   float scale_log2;  // scale * log2(e)
   float tau;
   unsigned* events;  // counting instantiation: corrections per (b, h, 32-row slot), added to
@@ -105,8 +106,8 @@ constexpr int kAhead = 4;   // MFMA operand fragments in flight per wave
 // (wavefront, tile) steps after the wavefront's first tile in which the
 // correction branch was taken to p.events[(b H + h) n_slots + i] (in the
 // split form both wave groups of those rows add to the slot).
-template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT = false>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
+template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT>
+__device__ __forceinline__ void fwd_block(const FwdParams& p, const int rank, const int bh) {
   using L = FwdLayout<D, SPLIT>;
   constexpr int kBN = L::kBN;
   constexpr int kKB = kBN / 32;   // 32-key blocks per tile
@@ -115,17 +116,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   constexpr int kKC = D / 16;     // 16-dim steps of Q K^T
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x;
+  // opaque per block, so that nothing derived from the lane index is hoisted
+  // out of the paired launch's loop and held live across a whole block
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  // heaviest causal query blocks first; consecutive workgroups take different
-  // heads of the same block rank
-  const int rank = blockIdx.x / p.BH;
-  const int bh = blockIdx.x % p.BH;
+  // rank 0 is the heaviest causal query block
   const int qb = CAUSAL ? (p.n_qblocks - 1 - rank) : rank;
 
   // key indices below are local to the range (key j is global key k_begin + j)
@@ -554,6 +555,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   }
 }
 
+// One query block per workgroup, heaviest causal blocks first (consecutive
+// workgroups take different heads of the same block rank); or, paired,
+// workgroup (r, bh) runs rank r and then rank n_qblocks - 1 - r of the same
+// head: every workgroup has the same causal work and the CU starts no new
+// workgroup between the two blocks.  Between them every wave's loads,
+// stores and LDS reads have completed (the second block's prologue loads
+// into the LDS the first one's epilogue staged its output in).
+template <int D, bool CAUSAL, int EMU, bool SPLIT, bool COUNT = false>
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
+  const int r = blockIdx.x / p.BH, bh = blockIdx.x % p.BH;
+  int n_it = p.paired ? 2 : 1;
+  asm volatile("" : "+s"(n_it));
+#pragma unroll 1
+  for (int it = 0; it < n_it; ++it) {
+    if (it > 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fwd_block<D, CAUSAL, EMU, SPLIT, COUNT>(p, it == 0 ? r : p.n_qblocks - 1 - r, bh);
+  }
+}
+
 // Software-exponential counts per 32 scores of a lane (64 keys) that are
 // instantiated.
 constexpr int kEmuCounts[] = {0, 3, 8, 16, 32};
@@ -624,7 +644,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.causal && full_blocks < kSplitBelowBlocks;
   const int rows = split ? kBM / 2 : kBM;
   prm.n_qblocks = (a.Sq + rows - 1) / rows;
-  const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
+  prm.paired = (a.causal && prm.n_qblocks % 2 == 0) ? 1 : 0;
+  const dim3 grid((unsigned)((prm.paired ? prm.n_qblocks / 2 : prm.n_qblocks) * prm.BH));
   if (a.d == 64) {
     if (!a.causal) return launch_d_causal<64, false, false>(prm, a.emu_count, grid, stream);
     return split ? launch_d_causal<64, true, true>(prm, a.emu_count, grid, stream)
