@@ -42,6 +42,10 @@ def check_partial(o, lse, O, L, what):
     (100, 300, 0, 0, 300, False), (100, 300, 0, 37, 250, False), (77, 300, 0, 250, 300, False),
     (128, 512, 200, 0, 64, True), (128, 512, 200, 64, 230, True), (128, 512, 200, 230, 512, True),
     (300, 300, 0, 0, 300, True), (300, 300, 0, 129, 300, True), (513, 1024, 511, 700, 1024, True),
+    # an even number of 128-row query blocks: the causal launch pairs block 3 with 0 and 2 with
+    # 1 in one workgroup each; with keys 300.. rows 0-255 see none, so the second block of
+    # each pair is one with no visible key (the early exit between two blocks)
+    (512, 1024, 0, 300, 1024, True), (512, 512, 0, 0, 512, True),
 ])
 def test_partial_every_element(d, Sq, Sk, q_off, kb, ke, causal):
     say(f"partial d={d} Sq={Sq} Sk={Sk} q_off={q_off} keys {kb}..{ke} causal={causal}")
