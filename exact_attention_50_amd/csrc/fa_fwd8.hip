@@ -66,6 +66,7 @@ struct Fwd8Params {
   bf16* o;
   float* lse;
   int BH, Sq, Sk, n_qblocks;
+  int paired;        // causal, n_qblocks even: workgroup (r, bh) runs ranks r and n_qblocks - 1 - r
   float s_log2;      // scale * q_descale * k_descale * log2(e) (MXFP4: scale * log2(e))
   float v_descale;
   const float* hd;   // null, or per-slice factors [3][BH] (q, k, v)
@@ -193,8 +194,8 @@ __device__ __forceinline__ void dma_tile4(__amdgpu_buffer_rsrc_t src, __amdgpu_b
 // rounds r P to e4m3, r = its V factor / the head's largest, sums P itself
 // for the row sum (the tile's partial sums times 1 / r), and the epilogue
 // multiplies O by the largest factor.
-template <bool CAUSAL, bool FP4QK = false, bool BS = false, int D8 = 128>
-__global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
+template <bool CAUSAL, bool FP4QK, bool BS, int D8>
+__device__ __forceinline__ void fwd8_block(const Fwd8Params& p, const int rank, const int bh) {
   static_assert(!(FP4QK && BS), "block factors are for the e4m3 operands");
   static_assert(D8 == 128 || (D8 == 64 && !FP4QK), "head dimension 128, or 64 with e4m3 operands");
   constexpr int kTileD = kBN8 * D8;   // bytes of an e4m3 K or V tile
@@ -207,15 +208,16 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   constexpr int kNK = kKB * kKC;   // K Q^T products per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x;
+  // opaque per block, so that nothing derived from the lane index is hoisted
+  // out of the paired launch's loop and held live across a whole block
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  const int rank = blockIdx.x / p.BH;
-  const int bh = blockIdx.x % p.BH;
   float s_log2 = p.s_log2, v_descale = p.v_descale;
   if (p.hd) {
     s_log2 *= p.hd[bh] * p.hd[p.BH + bh];
@@ -570,6 +572,23 @@ __global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
   if (q_lane < p.Sq && g == 0) p.lse[(size_t)bh * p.Sq + q_lane] = (m_ref + __builtin_log2f(l)) * kLn2;
 }
 
+// One query block per workgroup, heaviest causal blocks first; or, paired,
+// workgroup (r, bh) runs rank r and then rank n_qblocks - 1 - r of the same
+// head (equal causal work per workgroup, no new workgroup between the two
+// blocks).  Between them every wave's loads, stores and LDS reads have
+// completed.
+template <bool CAUSAL, bool FP4QK = false, bool BS = false, int D8 = 128>
+__global__ __launch_bounds__(kThreads8, 1) void fwd8_kernel(Fwd8Params p) {
+  const int r = blockIdx.x / p.BH, bh = blockIdx.x % p.BH;
+  int n_it = p.paired ? 2 : 1;
+  asm volatile("" : "+s"(n_it));
+#pragma unroll 1
+  for (int it = 0; it < n_it; ++it) {
+    if (it > 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fwd8_block<CAUSAL, FP4QK, BS, D8>(p, it == 0 ? r : p.n_qblocks - 1 - r, bh);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
@@ -599,7 +618,8 @@ hipError_t launch_fwd_fp8(const FwdFp8Args& a, hipStream_t stream) {
     prm.v_descale = 1.0f;
     prm.hd = nullptr;
   }
-  const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
+  prm.paired = (a.causal && prm.n_qblocks % 2 == 0) ? 1 : 0;
+  const dim3 grid((unsigned)((prm.paired ? prm.n_qblocks / 2 : prm.n_qblocks) * prm.BH));
   auto run = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds8);
@@ -634,7 +654,8 @@ hipError_t launch_fwd_mxfp4(const FwdFp8Args& a, hipStream_t stream) {
   prm.tau = a.tau;
   prm.qbs = prm.kbs = prm.vbs = nullptr;
   prm.nqb = prm.nkb = 0;
-  const dim3 grid((unsigned)(prm.n_qblocks * prm.BH));
+  prm.paired = (a.causal && prm.n_qblocks % 2 == 0) ? 1 : 0;
+  const dim3 grid((unsigned)((prm.paired ? prm.n_qblocks / 2 : prm.n_qblocks) * prm.BH));
   auto run = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds8);
