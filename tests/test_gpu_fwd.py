@@ -48,8 +48,9 @@ def test_small_shapes_every_element(d, Sq, Sk, causal):
 def test_full_blocks_every_element(d, S, causal):
     """Enough heads for 256-row workgroups with 128-key tiles (small shapes
     and the 16-head causal workloads run the split 128-row form instead).
-    S = 1000 leaves a ragged last tile and block; S = 1200 an odd number of
-    query blocks."""
+    S = 1000 leaves a ragged last tile and block, and its four query blocks
+    per head run as pairs (a heavy block and its mirror in one workgroup);
+    S = 1200 has an odd number of query blocks, one per workgroup."""
     say(f"fwd B1 H128 S{S} d{d} causal={causal} (256-row workgroups)")
     q, k, v = make_inputs(1, 128, S, S, d, seed=21 + d + S)
     o, lse = run_fwd(q, k, v, causal)
